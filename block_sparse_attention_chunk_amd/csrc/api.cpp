@@ -1,0 +1,314 @@
+// api.cpp -- the C ABI of libbsa: host-side validation, launch geometry and
+// workspace sizing.  Every entry point checks its arguments before touching
+// HIP, so argument errors are reported without a device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "bsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return BSA_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
+}
+
+size_t elem_size(int dtype) { return dtype == BSA_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every call that reads the cache.
+int check_kv(const bsa_kv *kv, bool need_v, bsa::KvView *view) {
+    if (!kv) return fail(BSA_ERR_INVALID_ARG, "kv is NULL");
+    if (!kv->k) return fail(BSA_ERR_INVALID_ARG, "kv->k is NULL");
+    if (need_v && !kv->v) return fail(BSA_ERR_INVALID_ARG, "kv->v is NULL");
+    if (!kv->seq_lens) return fail(BSA_ERR_INVALID_ARG, "kv->seq_lens is NULL");
+    if (kv->batch < 1 || kv->num_kv_heads < 1 || kv->max_pages < 1)
+        return fail(BSA_ERR_INVALID_ARG, "batch (%d), num_kv_heads (%d) and max_pages (%d) must be >= 1", kv->batch,
+                    kv->num_kv_heads, kv->max_pages);
+    if (kv->dtype != BSA_F32 && kv->dtype != BSA_BF16)
+        return fail(BSA_ERR_UNSUPPORTED, "dtype %d is not BSA_F32 or BSA_BF16", kv->dtype);
+    if (kv->head_dim != 64 && kv->head_dim != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", kv->head_dim);
+    if (!is_pow2(kv->page_size) || kv->page_size > 256)
+        return fail(BSA_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 256]", kv->page_size);
+    const int64_t unit = 16 / (int64_t)elem_size(kv->dtype);
+    if (kv->stride_page <= 0 || kv->stride_head <= 0 || kv->stride_token <= 0 || kv->stride_page % unit ||
+        kv->stride_head % unit || kv->stride_token % unit)
+        return fail(BSA_ERR_INVALID_ARG, "strides must be positive multiples of %lld elements (16 bytes)",
+                    (long long)unit);
+    if (!aligned16(kv->k) || (kv->v && !aligned16(kv->v)))
+        return fail(BSA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    if (view) {
+        *view = bsa::KvView{kv->k, kv->v, kv->stride_page, kv->stride_head, kv->stride_token, kv->block_table,
+                            kv->seq_lens, kv->batch, kv->num_kv_heads, kv->head_dim, kv->page_size,
+                            log2i(kv->page_size), kv->max_pages, kv->dtype};
+    }
+    return BSA_OK;
+}
+
+int check_chunks(const bsa_kv *kv, const bsa_chunks *ch, bsa::ChunkView *view) {
+    if (ch && ch->chunk_starts) {
+        if (!ch->num_chunks) return fail(BSA_ERR_INVALID_ARG, "chunks->num_chunks is NULL");
+        if (ch->max_chunks < 1) return fail(BSA_ERR_INVALID_ARG, "chunks->max_chunks must be >= 1");
+        *view = bsa::ChunkView{ch->chunk_starts, ch->num_chunks, ch->max_chunks};
+    } else {
+        *view = bsa::ChunkView{nullptr, nullptr, kv->max_pages};
+    }
+    return BSA_OK;
+}
+
+int check_heads(const bsa_kv *kv, int32_t num_q_heads, int max_group) {
+    if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads)
+        return fail(BSA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                    kv->num_kv_heads);
+    if (num_q_heads / kv->num_kv_heads > max_group)
+        return fail(BSA_ERR_UNSUPPORTED, "GQA group size %d exceeds %d", num_q_heads / kv->num_kv_heads, max_group);
+    return BSA_OK;
+}
+
+int launched(hipError_t e) {
+    if (e != hipSuccess) return fail(BSA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+constexpr int kMaxSelectChunks = 8192;
+constexpr int kMaxRouterBlocks = 8192;
+constexpr int kMaxRouterTiles = 8192;
+
+int resolve_splits(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
+    if (num_splits > 0) return num_splits;
+    const int bh = kv->batch * kv->num_kv_heads;
+    int s = (2048 + bh - 1) / bh;                       // aim at ~2048 workgroups (8 per CU)
+    const int cap = (max_items + 7) / 8;                // at least ~8 items per workgroup
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    if (s > 256) s = 256;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bsa_status_string(int32_t status) {
+    switch (status) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARG: return "BSA_ERR_INVALID_ARG";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_WORKSPACE: return "BSA_ERR_WORKSPACE";
+    case BSA_ERR_LAUNCH: return "BSA_ERR_LAUNCH";
+    default: return "BSA_ERR_UNKNOWN";
+    }
+}
+
+const char *bsa_last_error(void) { return g_err; }
+
+int bsa_build_chunk_meta(const bsa_kv *kv, const bsa_chunks *chunks, const bsa_meta *meta, uint32_t which,
+                         void *stream) {
+    bsa::KvView v;
+    bsa::ChunkView c;
+    int rc = check_kv(kv, false, &v);
+    if (rc) return rc;
+    if ((rc = check_chunks(kv, chunks, &c))) return rc;
+    if (!meta) return fail(BSA_ERR_INVALID_ARG, "meta is NULL");
+    if (which == 0 || (which & ~(BSA_META_ENVELOPE | BSA_META_CENTROID)))
+        return fail(BSA_ERR_INVALID_ARG, "which must be a non-empty combination of BSA_META_* bits");
+    if ((which & BSA_META_ENVELOPE) && (!meta->kmin || !meta->kmax))
+        return fail(BSA_ERR_INVALID_ARG, "meta->kmin / kmax is NULL");
+    if ((which & BSA_META_CENTROID) && !meta->centroid) return fail(BSA_ERR_INVALID_ARG, "meta->centroid is NULL");
+    return launched(bsa::launch_chunk_meta(v, c, meta->kmin, meta->kmax, meta->centroid, which, (hipStream_t)stream));
+}
+
+int bsa_score_chunks(const void *q, int32_t num_q_heads, int32_t num_rows, int32_t rows_per_query, const bsa_kv *kv,
+                     const bsa_chunks *chunks, const bsa_meta *meta, int32_t score_kind, int32_t causal,
+                     float *scores, void *stream) {
+    bsa::KvView v;
+    bsa::ChunkView c;
+    int rc = check_kv(kv, false, &v);
+    if (rc) return rc;
+    if ((rc = check_chunks(kv, chunks, &c))) return rc;
+    if (!q || !scores || !meta) return fail(BSA_ERR_INVALID_ARG, "q, scores and meta must be non-NULL");
+    if (!aligned16(q)) return fail(BSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if (score_kind != BSA_ENVELOPE && score_kind != BSA_CENTROID)
+        return fail(BSA_ERR_INVALID_ARG, "score_kind %d is not BSA_ENVELOPE or BSA_CENTROID", score_kind);
+    if (score_kind == BSA_ENVELOPE && (!meta->kmin || !meta->kmax))
+        return fail(BSA_ERR_INVALID_ARG, "envelope scoring needs meta->kmin and meta->kmax");
+    if (score_kind == BSA_CENTROID && !meta->centroid)
+        return fail(BSA_ERR_INVALID_ARG, "centroid scoring needs meta->centroid");
+    if (rows_per_query < 1) return fail(BSA_ERR_INVALID_ARG, "rows_per_query must be >= 1");
+    if (rows_per_query == 1) {
+        if ((rc = check_heads(kv, num_q_heads, 16))) return rc;
+        if (num_rows != kv->batch)
+            return fail(BSA_ERR_INVALID_ARG, "decode scoring needs num_rows (%d) == batch (%d)", num_rows, kv->batch);
+        return launched(bsa::launch_score_decode(q, num_q_heads, v, c, meta->kmin, meta->kmax, meta->centroid,
+                                                 score_kind, scores, (hipStream_t)stream));
+    }
+    if ((rc = check_heads(kv, num_q_heads, 8))) return rc;
+    if (kv->dtype != BSA_BF16 || kv->head_dim != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "tile scoring supports bf16 with head_dim 128");
+    if (rows_per_query != 64) return fail(BSA_ERR_UNSUPPORTED, "tile scoring supports 64-row tiles");
+    if (kv->batch != 1) return fail(BSA_ERR_INVALID_ARG, "tile scoring needs batch == 1");
+    if (chunks && chunks->chunk_starts) return fail(BSA_ERR_UNSUPPORTED, "tile scoring uses fixed key blocks");
+    if (causal && kv->page_size != rows_per_query)
+        return fail(BSA_ERR_UNSUPPORTED, "causal tile scoring needs block size == rows_per_query");
+    if (num_rows < 1) return fail(BSA_ERR_INVALID_ARG, "num_rows must be >= 1");
+    return launched(bsa::launch_score_tiles(q, num_q_heads, num_rows, rows_per_query, v, kv->max_pages, meta->kmin,
+                                            meta->kmax, meta->centroid, score_kind, causal, scores,
+                                            (hipStream_t)stream));
+}
+
+int bsa_select_topk(const float *scores, const bsa_kv *kv, const bsa_chunks *chunks, const bsa_budget *budget,
+                    int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *stream) {
+    bsa::KvView v;
+    bsa::ChunkView c;
+    int rc = check_kv(kv, false, &v);
+    if (rc) return rc;
+    if ((rc = check_chunks(kv, chunks, &c))) return rc;
+    if (!scores || !budget || !sel_idx || !sel_count)
+        return fail(BSA_ERR_INVALID_ARG, "scores, budget, sel_idx and sel_count must be non-NULL");
+    if (c.max_chunks > kMaxSelectChunks)
+        return fail(BSA_ERR_UNSUPPORTED, "max_chunks %d exceeds %d", c.max_chunks, kMaxSelectChunks);
+    if (max_sel < 1) return fail(BSA_ERR_INVALID_ARG, "max_sel must be >= 1");
+    int64_t need;
+    switch (budget->mode) {
+    case BSA_BUDGET_TOPK:
+        if (budget->top_k < 1) return fail(BSA_ERR_INVALID_ARG, "top_k must be >= 1");
+        need = budget->top_k < c.max_chunks ? budget->top_k : c.max_chunks;
+        break;
+    case BSA_BUDGET_TOKENS:
+        if (budget->tokens < 1) return fail(BSA_ERR_INVALID_ARG, "tokens must be >= 1");
+        need = budget->tokens < c.max_chunks ? budget->tokens : c.max_chunks;
+        break;
+    case BSA_BUDGET_RATIO: {
+        if (!(budget->ratio > 0.0 && budget->ratio <= 1.0))
+            return fail(BSA_ERR_INVALID_ARG, "ratio must be in (0, 1]");
+        if ((budget->bos != 0 && budget->bos != 1) || (budget->eos != 0 && budget->eos != 1))
+            return fail(BSA_ERR_INVALID_ARG, "bos and eos must be 0 or 1");
+        int64_t K = (int64_t)std::floor((double)c.max_chunks * budget->ratio);
+        const int64_t forced = 1 + budget->bos + budget->eos;
+        if (K < forced) K = forced;
+        need = K < c.max_chunks ? K : c.max_chunks;
+        break;
+    }
+    default:
+        return fail(BSA_ERR_INVALID_ARG, "budget mode %d is not a BSA_BUDGET_* value", budget->mode);
+    }
+    if (max_sel < need)
+        return fail(BSA_ERR_INVALID_ARG, "max_sel %d is smaller than the largest possible selection %lld", max_sel,
+                    (long long)need);
+    return launched(bsa::launch_select(scores, v, c, *budget, sel_idx, sel_count, max_sel, (hipStream_t)stream));
+}
+
+size_t bsa_router_workspace_bytes(int32_t num_tiles, int32_t num_kv_heads, int32_t k, int32_t rho) {
+    if (num_tiles < 1 || num_kv_heads < 1 || k < 1 || rho < 1) return 0;
+    return (size_t)num_tiles * num_kv_heads * k * rho * sizeof(int32_t);
+}
+
+int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t num_kv_heads, int32_t num_blocks,
+                           int32_t causal, int32_t k, int32_t rho, float quantile, float fixed_threshold,
+                           int32_t *kv_idx, float *sigma, float *sigma_bar, uint8_t *triggered, float *threshold,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (!tile_scores || !kv_idx || !sigma || !sigma_bar || !triggered || !threshold)
+        return fail(BSA_ERR_INVALID_ARG, "tile_scores and every output pointer must be non-NULL");
+    if (num_tiles < 1 || num_kv_heads < 1 || num_blocks < 1 || k < 1 || rho < 1)
+        return fail(BSA_ERR_INVALID_ARG, "num_tiles, num_kv_heads, num_blocks, k and rho must be >= 1");
+    const int want = (rho * k > k + 1) ? rho * k : k + 1;
+    if (want > 256) return fail(BSA_ERR_UNSUPPORTED, "max(rho*k, k+1) = %d exceeds 256", want);
+    if (num_blocks > kMaxRouterBlocks) return fail(BSA_ERR_UNSUPPORTED, "num_blocks %d exceeds %d", num_blocks,
+                                                   kMaxRouterBlocks);
+    if (num_tiles > kMaxRouterTiles)
+        return fail(BSA_ERR_UNSUPPORTED, "num_tiles %d exceeds %d", num_tiles, kMaxRouterTiles);
+    if (std::isnan(fixed_threshold) && !(quantile >= 0.f && quantile <= 1.f))
+        return fail(BSA_ERR_INVALID_ARG, "quantile must be in [0, 1]");
+    const size_t need = bsa_router_workspace_bytes(num_tiles, num_kv_heads, k, rho);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSA_ERR_WORKSPACE, "router workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    return launched(bsa::launch_router(tile_scores, num_tiles, num_kv_heads, num_blocks, causal, k, rho, quantile,
+                                       fixed_threshold, kv_idx, sigma, sigma_bar, triggered, threshold, workspace,
+                                       (hipStream_t)stream));
+}
+
+int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits) {
+    (void)num_q_heads;
+    if (!kv || kv->batch < 1 || kv->num_kv_heads < 1 || max_items < 1) return 1;
+    return resolve_splits(kv, max_items, num_splits);
+}
+
+size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits) {
+    const int s = bsa_decode_num_splits(kv, num_q_heads, max_items, num_splits);
+    if (s <= 1 || !kv) return 0;
+    return (size_t)kv->batch * num_q_heads * s * (kv->head_dim + 2) * sizeof(float);
+}
+
+int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_chunks *chunks,
+                           const int32_t *sel_idx, const int32_t *sel_count, int32_t max_sel, float softmax_scale,
+                           int32_t num_splits, float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    bsa::KvView v;
+    bsa::ChunkView c;
+    int rc = check_kv(kv, true, &v);
+    if (rc) return rc;
+    if ((rc = check_chunks(kv, chunks, &c))) return rc;
+    if ((rc = check_heads(kv, num_q_heads, 16))) return rc;
+    if (!q || !out) return fail(BSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if (!aligned16(q)) return fail(BSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if (sel_idx && (!sel_count || max_sel < 1))
+        return fail(BSA_ERR_INVALID_ARG, "sel_idx needs sel_count and max_sel >= 1");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+        return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+    if (num_splits < 0) return fail(BSA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    const int items = sel_idx ? max_sel : c.max_chunks;
+    const int splits = resolve_splits(kv, items, num_splits);
+    const size_t need = bsa_decode_workspace_bytes(kv, num_q_heads, items, splits);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    return launched(bsa::launch_decode(q, num_q_heads, v, c, sel_idx, sel_count, max_sel, softmax_scale, splits, out,
+                                       workspace, (hipStream_t)stream));
+}
+
+int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num_rows, const bsa_kv *kv,
+                                 int32_t tile_rows, const int32_t *kv_idx, int32_t idx_stride, float softmax_scale,
+                                 float *out, void *stream) {
+    bsa::KvView v;
+    int rc = check_kv(kv, true, &v);
+    if (rc) return rc;
+    if ((rc = check_heads(kv, num_q_heads, 8))) return rc;
+    if (!q || !out) return fail(BSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if (!aligned16(q)) return fail(BSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if (kv->dtype != BSA_BF16 || kv->head_dim != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "tile prefill supports bf16 with head_dim 128");
+    if (kv->batch != 1 || kv->block_table)
+        return fail(BSA_ERR_UNSUPPORTED, "tile prefill needs batch 1 and a token-major cache (block_table NULL)");
+    if (tile_rows != 64 || kv->page_size != 64)
+        return fail(BSA_ERR_UNSUPPORTED, "tile prefill supports 64-row tiles over 64-token blocks");
+    if (num_rows < 1) return fail(BSA_ERR_INVALID_ARG, "num_rows must be >= 1");
+    if (kv_idx && idx_stride < 1) return fail(BSA_ERR_INVALID_ARG, "idx_stride must be >= 1");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+        return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+    return launched(bsa::launch_tile_prefill(q, num_q_heads, num_rows, v, tile_rows, kv_idx, idx_stride,
+                                             softmax_scale, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// bsa_internal.h -- device helpers and launcher declarations shared by the
+// libbsa HIP sources (gfx950 only).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bsa.h"
+
+namespace bsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- bf16 <-> f32 on raw bits ------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+// exact for values that are already representable in bf16 (min / max of bf16s)
+__device__ __forceinline__ uint16_t f32_to_bf16_exact(float x) { return uint16_t(__float_as_uint(x) >> 16); }
+// round to nearest even (finite values)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---- order-preserving float keys --------------------------------------------
+// key(a) < key(b)  <=>  a < b  for non-NaN floats (-0 sorts below +0).
+__device__ __forceinline__ uint32_t float_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+// ---- wave-level helpers (wave64) --------------------------------------------
+__device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- block-wide inclusive scans over 256 threads (4 waves) ------------------
+// Returns the inclusive prefix of v over threadIdx.x; *total gets the block sum.
+// `scratch` needs 8 ints of shared memory.  All 256 threads must call it.
+__device__ __forceinline__ int block_scan_incl_256(int v, int *scratch, int *total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) scratch[wid] = x;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        int s = scratch[w];
+        if (w < wid) off += s;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return x + off;
+}
+
+// ---- launchers (defined in the .hip files) -----------------------------------
+struct KvView {
+    const void *k, *v;
+    int64_t sp, sh, st;
+    const int32_t *bt;
+    const int32_t *seq_lens;
+    int32_t batch, hkv, d, page, log2page, max_pages, dtype;
+};
+
+struct ChunkView {
+    const int32_t *starts;   // NULL = fixed pages
+    const int32_t *num;
+    int32_t max_chunks;
+};
+
+hipError_t launch_chunk_meta(const KvView &kv, const ChunkView &ch, void *kmin, void *kmax, float *cen,
+                             uint32_t which, hipStream_t s);
+hipError_t launch_score_decode(const void *q, int32_t hq, const KvView &kv, const ChunkView &ch, const void *kmin,
+                               const void *kmax, const float *cen, int32_t kind, float *scores, hipStream_t s);
+hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t tile_rows, const KvView &kv,
+                              int32_t n_blocks, const void *kmin, const void *kmax, const float *cen, int32_t kind,
+                              int32_t causal, float *scores, hipStream_t s);
+hipError_t launch_select(const float *scores, const KvView &kv, const ChunkView &ch, const bsa_budget &b,
+                         int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, hipStream_t s);
+hipError_t launch_router(const float *ts, int32_t n_tiles, int32_t hkv, int32_t n_blocks, int32_t causal, int32_t k,
+                         int32_t rho, float quantile, float fixed, int32_t *kv_idx, float *sigma, float *sigma_bar,
+                         uint8_t *triggered, float *threshold, void *ws, hipStream_t s);
+hipError_t launch_decode(const void *q, int32_t hq, const KvView &kv, const ChunkView &ch, const int32_t *sel_idx,
+                         const int32_t *sel_count, int32_t max_sel, float scale, int32_t splits, float *out,
+                         void *ws, hipStream_t s);
+hipError_t launch_tile_prefill(const void *q, int32_t hq, int32_t rows, const KvView &kv, int32_t tile_rows,
+                               const int32_t *kv_idx, int32_t idx_stride, float scale, float *out, hipStream_t s);
+
+}  // namespace bsa

@@ -1,0 +1,309 @@
+// score.hip -- chunk scoring against the current query (decode) and against
+// query tiles (prefill).
+//
+// Source: "Sparse Attention for Web Agents -- Offline Replay Records",
+// section "The comparison" (envelope = per-dimension min/max upper bound,
+// centroid = mean of chunk keys); "Technische Samenvatting ... Blok-schaarse
+// Aandacht", section "Methodologie" steps 1-2 (the tile score is the maximum
+// over the tile's query rows).  Selection is per KV head, so the scores of a
+// GQA group's query heads are combined by their maximum.
+#include "bsa_internal.h"
+
+namespace bsa {
+
+// ---------------------------------------------------------------------------
+// Decode: one thread per chunk, the GQA group's query in LDS.
+// Envelope per head: sum_d max(q*kmin, q*kmax) = sum_d (q+ * kmax + q- * kmin)
+// with q+ = max(q, 0), q- = min(q, 0): two FMAs per element, one of them a
+// multiply by an exact zero, so each term is rounded once.  HBM-bound on the
+// metadata read (512 B per chunk and KV head at d = 128).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int GP, int KIND>
+__global__ __launch_bounds__(256) void score_decode_kernel(const T *__restrict__ q, int hq, KvView kv, ChunkView ch,
+                                                           const T *__restrict__ kmin, const T *__restrict__ kmax,
+                                                           const float *__restrict__ cen, float *__restrict__ out) {
+    constexpr int NQ = KIND == BSA_ENVELOPE ? 2 * GP : GP;  // floats per dim in LDS
+    __shared__ float qs[D * NQ];
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = hq / kv.hkv;
+    for (int i = threadIdx.x; i < D * GP; i += blockDim.x) {
+        const int d = i / GP, j = i % GP;
+        float x = 0.f;
+        if (j < g) {
+            const T *qr = q + ((int64_t)b * hq + h * g + j) * D + d;
+            if constexpr (sizeof(T) == 2)
+                x = bf16_to_f32(*reinterpret_cast<const uint16_t *>(qr));
+            else
+                x = *reinterpret_cast<const float *>(qr);
+        }
+        if constexpr (KIND == BSA_ENVELOPE) {
+            qs[d * NQ + j] = fmaxf(x, 0.f);
+            qs[d * NQ + GP + j] = fminf(x, 0.f);
+        } else {
+            qs[d * NQ + j] = x;
+        }
+    }
+    __syncthreads();
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= ch.max_chunks) return;
+    const int n = ch.starts ? ch.num[b] : (kv.seq_lens[b] + kv.page - 1) >> kv.log2page;
+    const int64_t orow = ((int64_t)b * kv.hkv + h) * ch.max_chunks + c;
+    if (c >= n) {
+        out[orow] = -INFINITY;
+        return;
+    }
+    float acc[GP];
+#pragma unroll
+    for (int j = 0; j < GP; ++j) acc[j] = 0.f;
+    const int64_t mrow = orow * D;
+    if constexpr (KIND == BSA_ENVELOPE) {
+        constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte load
+        const uint4 *pmin = reinterpret_cast<const uint4 *>(kmin + mrow);
+        const uint4 *pmax = reinterpret_cast<const uint4 *>(kmax + mrow);
+#pragma unroll 2
+        for (int v = 0; v < D / EPV; ++v) {
+            const uint4 wmin = pmin[v], wmax = pmax[v];
+            float lo[EPV], hi[EPV];
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t a[4] = {wmin.x, wmin.y, wmin.z, wmin.w}, bb[4] = {wmax.x, wmax.y, wmax.z, wmax.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[2 * i] = bf16_lo(a[i]);
+                    lo[2 * i + 1] = bf16_hi(a[i]);
+                    hi[2 * i] = bf16_lo(bb[i]);
+                    hi[2 * i + 1] = bf16_hi(bb[i]);
+                }
+            } else {
+                lo[0] = __uint_as_float(wmin.x); lo[1] = __uint_as_float(wmin.y);
+                lo[2] = __uint_as_float(wmin.z); lo[3] = __uint_as_float(wmin.w);
+                hi[0] = __uint_as_float(wmax.x); hi[1] = __uint_as_float(wmax.y);
+                hi[2] = __uint_as_float(wmax.z); hi[3] = __uint_as_float(wmax.w);
+            }
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const float *qd = qs + (v * EPV + e) * NQ;
+#pragma unroll
+                for (int j = 0; j < GP; ++j) {
+                    acc[j] = fmaf(qd[j], hi[e], acc[j]);
+                    acc[j] = fmaf(qd[GP + j], lo[e], acc[j]);
+                }
+            }
+        }
+    } else {
+        const float4 *pc = reinterpret_cast<const float4 *>(cen + mrow);
+#pragma unroll 4
+        for (int v = 0; v < D / 4; ++v) {
+            const float4 w = pc[v];
+            const float cv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *qd = qs + (v * 4 + e) * NQ;
+#pragma unroll
+                for (int j = 0; j < GP; ++j) acc[j] = fmaf(qd[j], cv[e], acc[j]);
+            }
+        }
+    }
+    float best = acc[0];
+#pragma unroll
+    for (int j = 1; j < GP; ++j)
+        if (j < g) best = fmaxf(best, acc[j]);
+    out[orow] = best;
+}
+
+template <typename T, int D, int KIND>
+static void dispatch_decode_g(const void *q, int hq, const KvView &kv, const ChunkView &ch, const void *kmin,
+                              const void *kmax, const float *cen, float *scores, hipStream_t s) {
+    const int g = hq / kv.hkv;
+    dim3 grid((ch.max_chunks + 255) / 256, kv.hkv, kv.batch), block(256);
+    const T *qq = (const T *)q;
+    const T *mn = (const T *)kmin;
+    const T *mx = (const T *)kmax;
+    if (g <= 4)
+        hipLaunchKernelGGL((score_decode_kernel<T, D, 4, KIND>), grid, block, 0, s, qq, hq, kv, ch, mn, mx, cen, scores);
+    else if (g <= 8)
+        hipLaunchKernelGGL((score_decode_kernel<T, D, 8, KIND>), grid, block, 0, s, qq, hq, kv, ch, mn, mx, cen, scores);
+    else
+        hipLaunchKernelGGL((score_decode_kernel<T, D, 16, KIND>), grid, block, 0, s, qq, hq, kv, ch, mn, mx, cen,
+                           scores);
+}
+
+template <typename T, int D>
+static void dispatch_decode_kind(const void *q, int hq, const KvView &kv, const ChunkView &ch, const void *kmin,
+                                 const void *kmax, const float *cen, int kind, float *scores, hipStream_t s) {
+    if (kind == BSA_ENVELOPE)
+        dispatch_decode_g<T, D, BSA_ENVELOPE>(q, hq, kv, ch, kmin, kmax, cen, scores, s);
+    else
+        dispatch_decode_g<T, D, BSA_CENTROID>(q, hq, kv, ch, kmin, kmax, cen, scores, s);
+}
+
+hipError_t launch_score_decode(const void *q, int32_t hq, const KvView &kv, const ChunkView &ch, const void *kmin,
+                               const void *kmax, const float *cen, int32_t kind, float *scores, hipStream_t s) {
+    if (kv.dtype == BSA_BF16) {
+        if (kv.d == 128) dispatch_decode_kind<uint16_t, 128>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);
+        else dispatch_decode_kind<uint16_t, 64>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);
+    } else {
+        if (kv.d == 128) dispatch_decode_kind<float, 128>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);
+        else dispatch_decode_kind<float, 64>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Query tiles on the matrix cores.  One workgroup per (tile t, KV head h),
+// one wave per query head of the group, 64 rows per wave (four 16-row MFMA
+// column tiles).  The block scores of a head form the product
+//     S^T[block][row] = sum_f A[block][f] * B[f][row]
+// over 2*D features: envelope A = [kmax | kmin], B = [q+ ; q-];
+// centroid A = [c_hi | c_lo] (float32 centroid split into two bf16 terms),
+// B = [q ; q].  bf16 inputs, fp32 accumulation (v_mfma_f32_16x16x32_bf16).
+// The wave's 64 rows are reduced by max in registers and across the 16 lanes
+// of a row group, the group's heads through LDS.  Metadata for 16 blocks is
+// staged in LDS and shared by all waves.
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 64;
+constexpr int kBlkTile = 16;               // blocks per MFMA row tile
+constexpr int kFeatRow = 2 * 128 + 8;      // staged bf16 features per block (+16 B pad)
+
+__device__ __forceinline__ uint4 split_sign(uint4 w, bool neg) {
+    // keep the bf16 halves whose sign matches (neg: negative halves, else the rest)
+    uint32_t in[4] = {w.x, w.y, w.z, w.w}, o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t spread = ((in[i] & 0x80008000u) >> 15) * 0xffffu;
+        o[i] = neg ? (in[i] & spread) : (in[i] & ~spread);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512) void score_tiles_kernel(const uint16_t *__restrict__ q, int hq, int rows,
+                                                          KvView kv, int n_blocks, const uint16_t *__restrict__ kmin,
+                                                          const uint16_t *__restrict__ kmax,
+                                                          const float *__restrict__ cen, int causal,
+                                                          float *__restrict__ out) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) uint16_t feat[kBlkTile * kFeatRow];
+    __shared__ float red[8][kBlkTile];
+    const int t = blockIdx.x, h = blockIdx.y;
+    const int g = hq / kv.hkv;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n16 = lane & 15, G = lane >> 4;
+    const int nthreads = blockDim.x;
+    const int r0 = t * kTileRows;
+    const int vis = causal ? min(n_blocks, (min(r0 + kTileRows, rows) - 1) / kv.page + 1) : n_blocks;
+    float *orow = out + ((int64_t)t * kv.hkv + h) * n_blocks;
+
+    // B operand: this wave's 64 rows (query head h*g + w), 8 k-steps of 32 features
+    bf16x8 bq[4][8];
+    bool rvalid[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int r = r0 + rt * 16 + n16;
+        rvalid[rt] = r < rows;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (rvalid[rt])
+                v = *reinterpret_cast<const uint4 *>(q + ((int64_t)r * hq + h * g + w) * D + 32 * s + 8 * G);
+            if constexpr (KIND == BSA_ENVELOPE) {
+                bq[rt][s] = __builtin_bit_cast(bf16x8, split_sign(v, false));
+                bq[rt][s + 4] = __builtin_bit_cast(bf16x8, split_sign(v, true));
+            } else {
+                bq[rt][s] = __builtin_bit_cast(bf16x8, v);
+                bq[rt][s + 4] = bq[rt][s];
+            }
+        }
+    }
+
+    const int64_t mbase = ((int64_t)h * n_blocks) * D;  // batch 1
+    const int ntiles16 = (vis + kBlkTile - 1) / kBlkTile;
+    for (int bt = 0; bt < ntiles16; ++bt) {
+        const int b0 = bt * kBlkTile;
+        // stage 16 blocks x 256 bf16 features
+        for (int i = threadIdx.x; i < kBlkTile * 32; i += nthreads) {
+            const int bl = i >> 5, part = i & 31;  // part: 16-byte piece of the 512-byte feature row
+            const int blk = b0 + bl;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (blk < vis) {
+                const int dpiece = part & 15;  // 8 dims
+                if constexpr (KIND == BSA_ENVELOPE) {
+                    const uint16_t *src = (part < 16 ? kmax : kmin) + mbase + (int64_t)blk * D + dpiece * 8;
+                    v = *reinterpret_cast<const uint4 *>(src);
+                } else {
+                    const float *src = cen + mbase + (int64_t)blk * D + dpiece * 8;
+                    const float4 a = reinterpret_cast<const float4 *>(src)[0];
+                    const float4 c = reinterpret_cast<const float4 *>(src)[1];
+                    const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+                    uint16_t o[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint16_t hb = f32_to_bf16_rne(x[e]);
+                        o[e] = part < 16 ? hb : f32_to_bf16_rne(x[e] - bf16_to_f32(hb));
+                    }
+                    v = make_uint4(o[0] | (uint32_t(o[1]) << 16), o[2] | (uint32_t(o[3]) << 16),
+                                   o[4] | (uint32_t(o[5]) << 16), o[6] | (uint32_t(o[7]) << 16));
+                }
+            }
+            *reinterpret_cast<uint4 *>(feat + bl * kFeatRow + part * 8) = v;
+        }
+        __syncthreads();
+        float bmax[4];
+        if (w < g) {
+            f32x4 acc[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(feat + n16 * kFeatRow + 32 * s + 8 * G);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[rt][s], acc[rt], 0, 0, 0);
+            }
+            // lane holds S^T[block 4G+i][row n16] of each row tile
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    if (rvalid[rt]) m = fmaxf(m, acc[rt][i]);
+                m = wave_max_xor(m, 1);
+                m = wave_max_xor(m, 2);
+                m = wave_max_xor(m, 4);
+                m = wave_max_xor(m, 8);
+                bmax[i] = m;
+            }
+            if (n16 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) red[w][4 * G + i] = bmax[i];
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < kBlkTile) {
+            const int blk = b0 + threadIdx.x;
+            if (blk < vis) {
+                float m = red[0][threadIdx.x];
+                for (int j = 1; j < g; ++j) m = fmaxf(m, red[j][threadIdx.x]);
+                orow[blk] = m;
+            }
+        }
+    }
+    for (int blk = vis + threadIdx.x; blk < n_blocks; blk += nthreads) orow[blk] = -INFINITY;
+}
+
+hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t tile_rows, const KvView &kv,
+                              int32_t n_blocks, const void *kmin, const void *kmax, const float *cen, int32_t kind,
+                              int32_t causal, float *scores, hipStream_t s) {
+    (void)tile_rows;  // validated to be 64 by the caller
+    const int g = hq / kv.hkv;
+    const int n_tiles = (rows + kTileRows - 1) / kTileRows;
+    dim3 grid(n_tiles, kv.hkv), block(64 * g);
+    if (kind == BSA_ENVELOPE)
+        hipLaunchKernelGGL((score_tiles_kernel<BSA_ENVELOPE>), grid, block, 0, s, (const uint16_t *)q, hq, rows, kv,
+                           n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal, scores);
+    else
+        hipLaunchKernelGGL((score_tiles_kernel<BSA_CENTROID>), grid, block, 0, s, (const uint16_t *)q, hq, rows, kv,
+                           n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal, scores);
+    return hipGetLastError();
+}
+
+}  // namespace bsa

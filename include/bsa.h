@@ -1,0 +1,247 @@
+/*
+ * bsa.h -- C ABI of libbsa: query-aware block-sparse attention over a chunked,
+ * paged GQA KV cache, hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * The method (cited by page title and section):
+ *  [P1] "Sparse Attention for Web Agents -- Offline Replay Records",
+ *       section "The comparison": chunk the KV cache, score every chunk against
+ *       the current query, keep the top-scoring chunks and attend only to them;
+ *       chunking is fixed 16-token pages (Quest, BlockSparse) or variable
+ *       16-256-token chunks (TSA); scoring is the per-dimension min/max
+ *       envelope (TSA, Quest) or the key centroid (BlockSparse); the budget is
+ *       page_size x top_k attended tokens.
+ *  [P2] "webarena" dataset README, section "Method configurations at a glance":
+ *       ratio budget max(topk_val + bos + eos, int(cached_block_len * ratio))
+ *       with forced first (bos) / last (eos) pages, topk_val = 1.
+ *  [P3] "Technische Samenvatting: Onzekerheidsgestuurde Selectie voor
+ *       Blok-schaarse Aandacht", section "Methodologie" steps 1-5: block
+ *       scoring, per-query-tile selection (tile score = max over the tile's
+ *       rows), the cut-off margin sigma, head averaging with a per-layer
+ *       quantile trigger, and expansion of triggered tiles to rho*k blocks with
+ *       sentinel padding so every tile has the same dispatch shape.
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE memory unless marked [host].  Structs passed by
+ *    pointer are read on the host during the call and may be freed after it.
+ *  - Every call validates its arguments on the host BEFORE any HIP call and
+ *    returns BSA_OK (0) or a negative BSA_ERR_* code; bsa_last_error() then
+ *    gives a thread-local description.  No exception crosses the ABI.
+ *  - Work is only enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream); no call synchronises.  Kernel faults surface at the caller's next
+ *    synchronisation.  Buffers must stay alive until the enqueued work ends.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    retains device memory; scratch comes in through `workspace`, sized by the
+ *    matching *_workspace_bytes() function.  Input values must be finite (not
+ *    checked).  Calls on distinct streams may run concurrently.
+ *  - All results are deterministic: no floating-point atomics are used.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define BSA_OK 0
+#define BSA_ERR_INVALID_ARG (-1)   /* a pointer, size or combination is invalid */
+#define BSA_ERR_UNSUPPORTED (-2)   /* valid but not implemented (dtype, head_dim, group size, ...) */
+#define BSA_ERR_WORKSPACE (-3)     /* workspace NULL or smaller than required */
+#define BSA_ERR_LAUNCH (-4)        /* the HIP runtime rejected a kernel launch */
+
+/* element types of K, V, Q and of the min/max metadata */
+#define BSA_F32 0
+#define BSA_BF16 1
+
+/* chunk scoring ([P1] method table) */
+#define BSA_ENVELOPE 0   /* sum_d max(q_d*kmin_d, q_d*kmax_d): Quest / TSA */
+#define BSA_CENTROID 1   /* q . mean(chunk keys): BlockSparse */
+
+/* which metadata bsa_build_chunk_meta writes (bit mask) */
+#define BSA_META_ENVELOPE 1u
+#define BSA_META_CENTROID 2u
+
+/* selection budgets */
+#define BSA_BUDGET_TOPK 0     /* keep top_k chunks ([P1] budget = page_size x top_k) */
+#define BSA_BUDGET_TOKENS 1   /* longest score-order prefix whose total length <= tokens */
+#define BSA_BUDGET_RATIO 2    /* [P2] ratio budget with forced bos / eos pages */
+
+/*
+ * A paged KV cache.  Element (physical page p, KV head h, slot o, dim d) of K
+ * (or V) is at k[p*stride_page + h*stride_head + o*stride_token + d] (strides in
+ * elements).  The default paged layout [n_pages][H_kv][page_size][D] has
+ * strides (H_kv*P*D, P*D, D): each (page, head) is one contiguous run.  A
+ * token-major cache [T][H_kv][D] cut into blocks of P tokens has strides
+ * (P*H_kv*D, D, H_kv*D).  Logical page j of sequence b is physical page
+ * block_table[b*max_pages + j]; block_table == NULL means b*max_pages + j.
+ * seq_lens [batch] holds each sequence's cached token count (device).
+ * Requirements: head_dim 64 or 128; page_size a power of two in [1, 256]
+ * (16 for the fastest decode path); k, v 16-byte aligned and every stride a
+ * multiple of 16 bytes / element size.
+ */
+typedef struct {
+    const void *k;
+    const void *v;
+    int64_t stride_page, stride_head, stride_token;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    int32_t batch, num_kv_heads, head_dim, page_size, max_pages, dtype;
+} bsa_kv;
+
+/*
+ * Variable chunking ([P1] TSA row: chunks aligned to document structure).
+ * chunk_starts [batch][max_chunks+1] token offsets (chunk c of sequence b is
+ * [starts[c], starts[c+1]) , increasing, starts[0] = 0, last = seq_len);
+ * num_chunks [batch].  Pass NULL (or a struct with chunk_starts NULL) for
+ * fixed pages: chunk c is page c, [c*P, min(c*P+P, L)), and max_chunks is
+ * kv->max_pages.
+ */
+typedef struct {
+    const int32_t *chunk_starts;
+    const int32_t *num_chunks;
+    int32_t max_chunks;
+} bsa_chunks;
+
+/* Per-chunk metadata, each [batch][H_kv][max_chunks][D]: kmin / kmax in the
+ * cache's element type (exact), centroid in float32.  A pointer may be NULL if
+ * the corresponding BSA_META_* bit / score kind is not used. */
+typedef struct {
+    void *kmin;
+    void *kmax;
+    float *centroid;
+} bsa_meta;
+
+/* Selection budget ([P1] "The comparison"; [P2] "Method configurations"). */
+typedef struct {
+    int32_t mode;      /* BSA_BUDGET_* */
+    int32_t top_k;     /* TOPK: chunks kept per (sequence, KV head) */
+    int64_t tokens;    /* TOKENS: attended-token budget */
+    int32_t bos, eos;  /* RATIO: force page 0 / the last page */
+    double ratio;      /* RATIO: topk_ratio */
+} bsa_budget;
+
+/*
+ * Step 1 ([P1] method table; [P3] step 1): per (sequence, KV head, chunk,
+ * dim), over the chunk's valid tokens: kmin = min K, kmax = max K,
+ * centroid = sum K / count (float32, tokens summed in order).  Chunks past a
+ * sequence's count are left untouched.  `which` = BSA_META_* bits.
+ * Layout: see bsa_meta.  Errors: INVALID_ARG (NULL pointer for a requested
+ * output, bad sizes), UNSUPPORTED (dtype, head_dim, page_size).
+ */
+int bsa_build_chunk_meta(const bsa_kv *kv, const bsa_chunks *chunks /* nullable */, const bsa_meta *meta,
+                         uint32_t which, void *stream);
+
+/*
+ * Step 2: chunk scores.  score_kind BSA_ENVELOPE or BSA_CENTROID ([P1]).
+ * Scores are raw dot products (no 1/sqrt(d)); for selection per KV head the
+ * scores of a GQA group's query heads are combined by their maximum.
+ *  - Decode (rows_per_query == 1): q [batch][H_q][D] (kv dtype, num_rows ==
+ *    batch); scores [batch][H_kv][max_chunks] float32, -inf past a sequence's
+ *    last chunk.
+ *  - Query tiles (rows_per_query == R > 1, [P3] step 2): kv->batch == 1,
+ *    token-major keys in blocks of kv->page_size tokens, q [num_rows][H_q][D]
+ *    bf16; tile t holds rows [t*R, t*R+R); its score for block b is the max
+ *    over the tile's rows and the group's heads.  With causal != 0 a tile only
+ *    sees blocks starting at or before its last row (requires R ==
+ *    page_size); other blocks get -inf.  scores [ceil(num_rows/R)][H_kv]
+ *    [max_chunks].  Computed on the matrix cores: the envelope as
+ *    [q+ | q-] x [kmax ; kmin], the centroid as q x [c_hi ; c_lo] with the
+ *    float32 centroid split into two bfloat16 terms (relative error ~2^-17).
+ * Errors: INVALID_ARG, UNSUPPORTED (group size > 16, head_dim, dtype).
+ */
+int bsa_score_chunks(const void *q, int32_t num_q_heads, int32_t num_rows, int32_t rows_per_query,
+                     const bsa_kv *kv, const bsa_chunks *chunks /* nullable */, const bsa_meta *meta,
+                     int32_t score_kind, int32_t causal, float *scores, void *stream);
+
+/*
+ * Step 3 (decode): per (sequence, KV head) selection from scores
+ * [batch][H_kv][max_chunks] under `budget` [host]. Candidates are ordered by
+ * score descending, lower chunk index first among equal scores.
+ *  TOPK:   the first min(top_k, n) chunks ([P1]).
+ *  RATIO:  K = min(n, max(1+bos+eos, floor(n*ratio))) with n the number of
+ *          cached pages; page 0 (bos) and page n-1 (eos) are always kept and
+ *          count inside K ([P2]).
+ *  TOKENS: the longest prefix of the order whose total token count <= tokens
+ *          (every chunk when the sequence fits).
+ * Output: sel_idx [batch][H_kv][max_sel] chunk ids ascending, -1 after the
+ * last; sel_count [batch][H_kv].  max_sel must hold the largest possible
+ * count (TOPK: min(top_k, max_chunks); RATIO: the formula at max_chunks;
+ * TOKENS: min(tokens, max_chunks)).  max_chunks <= 8192.
+ * Errors: INVALID_ARG (budget values, max_sel too small), UNSUPPORTED.
+ */
+int bsa_select_topk(const float *scores, const bsa_kv *kv, const bsa_chunks *chunks /* nullable */,
+                    const bsa_budget *budget /* [host] */, int32_t *sel_idx, int32_t *sel_count, int32_t max_sel,
+                    void *stream);
+
+/*
+ * Steps 2-5 of the uncertainty router ([P3] "Methodologie").
+ * tile_scores [num_tiles][H_kv][num_blocks] (e.g. from bsa_score_chunks with
+ * rows_per_query > 1).  Tile t sees n_t = min(t+1, num_blocks) blocks when
+ * causal (tile rows == block size), else num_blocks.  Per (tile, KV head),
+ * blocks are ordered by score (descending, lower index first) and
+ *   sigma = (s_(k-1) - s_(k)) / (s_(0) - s_(k))          (0-indexed, sorted)
+ * with sigma = 0 when s_(0) == s_(k) and sigma = 1 (tile not eligible) when
+ * n_t <= k.  sigma_bar[t] = mean over KV heads.  The threshold is the
+ * `quantile` quantile (linear interpolation between order statistics) of
+ * sigma_bar over eligible tiles, or fixed_threshold when it is not NaN;
+ * triggered[t] = eligible && sigma_bar[t] < threshold.  kv_idx[t][h] holds
+ * the first k blocks of the order (min(rho*k, n_t) when triggered),
+ * ascending, padded with -1 to rho*k entries.
+ * Outputs: kv_idx [num_tiles][H_kv][rho*k], sigma [num_tiles][H_kv],
+ * sigma_bar [num_tiles], triggered [num_tiles] (0/1), threshold [1].
+ * Limits: max(rho*k, k+1) <= 256, num_blocks <= 8192, num_tiles <= 8192.
+ * workspace >= bsa_router_workspace_bytes(...).
+ * Errors: INVALID_ARG, UNSUPPORTED (limits), WORKSPACE.
+ */
+size_t bsa_router_workspace_bytes(int32_t num_tiles, int32_t num_kv_heads, int32_t k, int32_t rho);
+int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t num_kv_heads, int32_t num_blocks,
+                           int32_t causal, int32_t k, int32_t rho, float quantile, float fixed_threshold,
+                           int32_t *kv_idx, float *sigma, float *sigma_bar, uint8_t *triggered, float *threshold,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Step 4 (decode, [P1] "attend only to those"): softmax(q K^T * scale) V over
+ * the tokens of the selected chunks only, for every query head; query head j
+ * reads KV head j / (H_q / H_kv).  Split-K: each (sequence, KV head) range of
+ * selected chunks is cut into num_splits parts (0 = automatic); each part
+ * runs an online softmax for the whole GQA group and the parts are merged.
+ * sel_idx [batch][H_kv][max_sel] / sel_count [batch][H_kv] as produced by
+ * bsa_select_topk; sel_idx == NULL attends to every chunk (dense baseline).
+ * q [batch][H_q][D] (kv dtype); out [batch][H_q][D] float32.
+ * Group size H_q/H_kv <= 16.  workspace >= bsa_decode_workspace_bytes(...)
+ * (0 bytes when the resolved split count is 1).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
+ */
+int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits);
+size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits);
+int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_chunks *chunks,
+                           const int32_t *sel_idx, const int32_t *sel_count, int32_t max_sel, float softmax_scale,
+                           int32_t num_splits, float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Step 5 attention ([P3] step 5): causal prefill over query tiles of
+ * tile_rows rows.  Row r of tile t, query head j, attends to the keys of the
+ * non-sentinel blocks in kv_idx[t][j / (H_q/H_kv)] (idx_stride entries per
+ * (tile, KV head), ascending, -1 padded) whose position is <= r;
+ * kv_idx == NULL attends to every block up to the diagonal (dense causal
+ * baseline).  kv: batch 1, token-major bf16 [num_rows][H_kv][D] with
+ * page_size == tile_rows == 64 and block_table NULL.  q [num_rows][H_q][D]
+ * bf16; out [num_rows][H_q][D] float32.  Matrix-core kernel (bf16 Q.K^T,
+ * fp16 P.V, fp32 accumulation).  Group size <= 8, head_dim 128.
+ * Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ */
+int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num_rows, const bsa_kv *kv,
+                                 int32_t tile_rows, const int32_t *kv_idx, int32_t idx_stride, float softmax_scale,
+                                 float *out, void *stream);
+
+/* Text for a status code, and the thread-local detail of the last failure. */
+const char *bsa_status_string(int32_t status);
+const char *bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

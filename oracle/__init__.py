@@ -92,7 +92,8 @@ def to_f64(x: np.ndarray) -> np.ndarray:
     (exact widening), float32 / float64 arrays are converted exactly."""
     x = np.asarray(x)
     if x.dtype == np.uint16:
-        return np.ascontiguousarray((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        with np.errstate(invalid="ignore"):
+            return np.ascontiguousarray((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
     return np.ascontiguousarray(x, dtype=np.float64)
 
 

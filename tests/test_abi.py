@@ -1,0 +1,169 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/bsa.h declares, and rejects invalid arguments on the host before any
+HIP call (so no GPU is needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_chunk_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 16-byte-aligned non-NULL address; never dereferenced by host validation
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_abi.SIGNATURES)
+
+
+def test_status_strings():
+    L = _abi.lib()
+    for code, name in [(0, "BSA_OK"), (-1, "BSA_ERR_INVALID_ARG"), (-2, "BSA_ERR_UNSUPPORTED"),
+                       (-3, "BSA_ERR_WORKSPACE"), (-4, "BSA_ERR_LAUNCH")]:
+        assert L.bsa_status_string(code).decode() == name
+
+
+def _kv(**over):
+    d = dict(k=FAKE, v=FAKE, stride_page=2 * 16 * 128, stride_head=16 * 128, stride_token=128, block_table=FAKE,
+             seq_lens=FAKE, batch=1, num_kv_heads=2, head_dim=128, page_size=16, max_pages=64, dtype=_abi.BSA_BF16)
+    d.update(over)
+    return _abi.bsa_kv(**d)
+
+
+def _decode(kv, hq=8, sel=True, scale=0.088, splits=1, ws=None, ws_bytes=0, max_sel=8, count=True):
+    L = _abi.lib()
+    return L.bsa_sparse_attn_decode(FAKE, hq, ctypes.byref(kv), None, FAKE if sel else None,
+                                    FAKE if count else None, max_sel, scale, splits, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(k=None), _abi.BSA_ERR_INVALID_ARG, "kv->k"),
+    (dict(v=None), _abi.BSA_ERR_INVALID_ARG, "kv->v"),
+    (dict(seq_lens=None), _abi.BSA_ERR_INVALID_ARG, "seq_lens"),
+    (dict(head_dim=96), _abi.BSA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(page_size=24), _abi.BSA_ERR_UNSUPPORTED, "page_size"),
+    (dict(page_size=512), _abi.BSA_ERR_UNSUPPORTED, "page_size"),
+    (dict(dtype=7), _abi.BSA_ERR_UNSUPPORTED, "dtype"),
+    (dict(k=FAKE + 2), _abi.BSA_ERR_INVALID_ARG, "aligned"),
+    (dict(stride_token=100), _abi.BSA_ERR_INVALID_ARG, "strides"),
+    (dict(batch=0), _abi.BSA_ERR_INVALID_ARG, "batch"),
+])
+def test_decode_rejects_bad_cache(over, code, msg):
+    L = _abi.lib()
+    assert _decode(_kv(**over)) == code
+    assert msg in L.bsa_last_error().decode()
+
+
+def test_decode_argument_checks():
+    L = _abi.lib()
+    assert _decode(_kv(), hq=7) == _abi.BSA_ERR_INVALID_ARG           # 7 % 2 != 0
+    assert _decode(_kv(), hq=34) == _abi.BSA_ERR_UNSUPPORTED          # group 17 > 16
+    assert _decode(_kv(), scale=0.0) == _abi.BSA_ERR_INVALID_ARG
+    assert _decode(_kv(), scale=math.inf) == _abi.BSA_ERR_INVALID_ARG
+    assert _decode(_kv(), count=False) == _abi.BSA_ERR_INVALID_ARG
+    assert _decode(_kv(), splits=-1) == _abi.BSA_ERR_INVALID_ARG
+    # 4 splits need a workspace of B*H_q*splits*(D+2)*4 bytes
+    need = L.bsa_decode_workspace_bytes(ctypes.byref(_kv()), 8, 8, 4)
+    assert need == 1 * 8 * 4 * 130 * 4
+    assert _decode(_kv(), splits=4) == _abi.BSA_ERR_WORKSPACE
+    assert _decode(_kv(), splits=4, ws=FAKE, ws_bytes=need - 1) == _abi.BSA_ERR_WORKSPACE
+    assert "workspace" in L.bsa_last_error().decode()
+
+
+def test_decode_split_resolution():
+    L = _abi.lib()
+    kv = _kv(batch=16, num_kv_heads=8)
+    assert L.bsa_decode_num_splits(ctypes.byref(kv), 64, 256, 0) == 16       # ~2048 workgroups
+    assert L.bsa_decode_num_splits(ctypes.byref(kv), 64, 256, 5) == 5        # explicit
+    kv1 = _kv(batch=1, num_kv_heads=4)
+    assert L.bsa_decode_num_splits(ctypes.byref(kv1), 32, 256, 0) == 32      # capped at ~8 items per workgroup
+    assert L.bsa_decode_num_splits(ctypes.byref(kv1), 32, 3, 0) == 1
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv1), 32, 3, 0) == 0
+
+
+def _select(kv, budget, max_sel, chunks=None):
+    L = _abi.lib()
+    return L.bsa_select_topk(FAKE, ctypes.byref(kv), chunks, ctypes.byref(budget), FAKE, FAKE, max_sel, None)
+
+
+def test_select_argument_checks():
+    kv = _kv()
+    B = _abi.bsa_budget
+    assert _select(kv, B(_abi.BSA_BUDGET_TOPK, 0, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_INVALID_ARG
+    assert _select(kv, B(_abi.BSA_BUDGET_TOPK, 16, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_INVALID_ARG  # max_sel < 16
+    assert _select(kv, B(_abi.BSA_BUDGET_RATIO, 0, 0, 1, 1, 0.0), 64) == _abi.BSA_ERR_INVALID_ARG
+    assert _select(kv, B(_abi.BSA_BUDGET_RATIO, 0, 0, 2, 1, 0.5), 64) == _abi.BSA_ERR_INVALID_ARG
+    # ratio 0.5 over 64 pages -> 32 kept; max_sel 31 is too small
+    assert _select(kv, B(_abi.BSA_BUDGET_RATIO, 0, 0, 1, 1, 0.5), 31) == _abi.BSA_ERR_INVALID_ARG
+    assert _select(kv, B(_abi.BSA_BUDGET_TOKENS, 0, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_INVALID_ARG
+    assert _select(kv, B(9, 1, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_INVALID_ARG
+    assert _select(_kv(max_pages=9000), B(_abi.BSA_BUDGET_TOPK, 4, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_UNSUPPORTED
+    ch = _abi.bsa_chunks(FAKE, None, 10)
+    assert _select(kv, B(_abi.BSA_BUDGET_TOPK, 4, 0, 0, 0, 0.0), 8, ctypes.byref(ch)) == _abi.BSA_ERR_INVALID_ARG
+
+
+def test_router_argument_checks():
+    L = _abi.lib()
+
+    def call(nt=8, H=2, nb=8, k=2, rho=2, quant=0.25, fixed=float("nan"), ws=FAKE, wsb=1 << 20):
+        return L.bsa_select_topk_router(FAKE, nt, H, nb, 1, k, rho, quant, fixed, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                        wsb, None)
+
+    assert L.bsa_router_workspace_bytes(2048, 4, 32, 2) == 2048 * 4 * 64 * 4
+    assert call(k=200, rho=2) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(k=256, rho=1) == _abi.BSA_ERR_UNSUPPORTED        # needs k+1 = 257 sorted scores
+    assert call(nb=9000) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(nt=9000) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(quant=1.5) == _abi.BSA_ERR_INVALID_ARG
+    assert call(k=0) == _abi.BSA_ERR_INVALID_ARG
+    assert call(ws=None) == _abi.BSA_ERR_WORKSPACE
+    assert call(wsb=8 * 2 * 4 * 4 - 1) == _abi.BSA_ERR_WORKSPACE
+
+
+def test_meta_and_score_argument_checks():
+    L = _abi.lib()
+    kv = _kv()
+    m = _abi.bsa_meta(FAKE, None, None)
+    assert L.bsa_build_chunk_meta(ctypes.byref(kv), None, ctypes.byref(m), _abi.BSA_META_ENVELOPE,
+                                  None) == _abi.BSA_ERR_INVALID_ARG
+    assert L.bsa_build_chunk_meta(ctypes.byref(kv), None, ctypes.byref(m), 0, None) == _abi.BSA_ERR_INVALID_ARG
+    assert L.bsa_build_chunk_meta(ctypes.byref(kv), None, None, 1, None) == _abi.BSA_ERR_INVALID_ARG
+    m2 = _abi.bsa_meta(FAKE, FAKE, None)
+    # centroid scoring without a centroid buffer
+    assert L.bsa_score_chunks(FAKE, 8, 1, 1, ctypes.byref(kv), None, ctypes.byref(m2), _abi.BSA_CENTROID, 0,
+                              FAKE, None) == _abi.BSA_ERR_INVALID_ARG
+    # decode scoring needs num_rows == batch
+    assert L.bsa_score_chunks(FAKE, 8, 3, 1, ctypes.byref(kv), None, ctypes.byref(m2), _abi.BSA_ENVELOPE, 0,
+                              FAKE, None) == _abi.BSA_ERR_INVALID_ARG
+    # tile scoring: 64-row tiles over 64-token blocks only
+    assert L.bsa_score_chunks(FAKE, 8, 128, 32, ctypes.byref(kv), None, ctypes.byref(m2), _abi.BSA_ENVELOPE, 1,
+                              FAKE, None) == _abi.BSA_ERR_UNSUPPORTED
+    kvt = _kv(page_size=64, stride_page=64 * 2 * 128, stride_head=128, stride_token=256, block_table=None)
+    assert L.bsa_score_chunks(FAKE, 18, 128, 64, ctypes.byref(kvt), None, ctypes.byref(m2), _abi.BSA_ENVELOPE, 1,
+                              FAKE, None) == _abi.BSA_ERR_UNSUPPORTED   # group 9 > 8
+
+
+def test_tile_prefill_argument_checks():
+    L = _abi.lib()
+    kvt = _kv(page_size=64, stride_page=64 * 2 * 128, stride_head=128, stride_token=256, block_table=None)
+    call = lambda kv, hq=8, tile=64, stride=4, idx=FAKE: L.bsa_sparse_attn_tile_prefill(
+        FAKE, hq, 256, ctypes.byref(kv), tile, idx, stride, 0.088, FAKE, None)
+    assert call(_kv()) == _abi.BSA_ERR_UNSUPPORTED                    # paged with a block table
+    assert call(kvt, tile=32) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(kvt, hq=18) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(kvt, stride=0) == _abi.BSA_ERR_INVALID_ARG
+    assert call(_kv(page_size=64, stride_page=64 * 2 * 128, stride_head=128, stride_token=256, block_table=None,
+                    dtype=_abi.BSA_F32, head_dim=128)) == _abi.BSA_ERR_UNSUPPORTED

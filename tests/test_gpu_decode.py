@@ -1,0 +1,205 @@
+"""GPU-vs-oracle parity of the decode path (metadata, scores, selection,
+split-K attention, dense baseline) through the C ABI.
+
+Workloads: the tiny fp32 decode; the 32:4-head, d 128 replay-shaped decode at
+29,504 tokens (budgets 4096 / 8192, envelope and centroid); the same with
+variable 16-256-token chunks (token budgets 4096 / 8192 / 16384 plus full
+context, and a 16,384-token instance whose 16,384 budget is dense); batched
+64:8-head decode with ragged lengths and the seven ratio budgets; NaN in the
+unused tail slots of partial pages; several split counts.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_attention_chunk_amd import synth
+from parity_lib import (ATTN_ABS, check_band, check_scores, gpu_kv, log, max_abs, oracle_cache, oracle_select)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_attention_chunk_amd import _abi
+    _abi.lib()
+    return torch.device("cuda:0")
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def run_decode_case(case, dev, kind, budget, forced=(), splits=(0,), check_dense=True, band_exact_count=True):
+    from block_sparse_attention_chunk_amd import ops
+    log(f"case {case.name} kind={kind} budget={budget}")
+    kv, chunks = gpu_kv(case, dev)
+    q = ops.upload(case.q, dev)
+    meta = ops.build_chunk_meta(kv, chunks)
+    scores = ops.score_chunks(q, kv, meta, kind, chunks=chunks)
+    sel, cnt = ops.select_topk(scores, kv, budget, chunks)
+    outs = {s: ops.sparse_attn_decode(q, kv, sel, cnt, chunks, num_splits=s) for s in splits}
+    dense = ops.sparse_attn_decode(q, kv, None, None, chunks) if check_dense else None
+    torch.cuda.synchronize()
+    kmin, kmax, cen = _np(meta.kmin), _np(meta.kmax), _np(meta.centroid)
+    scores, sel, cnt = _np(scores), _np(sel), _np(cnt)
+
+    oc = oracle_cache(case)
+    omin, omax, ocen = oracle.chunk_meta(oc, case.chunk_starts, case.num_chunks)
+    n = case.n_chunks()
+    wide = oracle.to_f64
+    # 1. metadata: min / max bit-exact, centroid within the fp32 summation bound
+    kabs = float(np.nanmax(np.abs(wide(case.k))))
+    nmax = int(np.max(np.diff(case.chunk_starts, axis=1))) if case.chunk_starts is not None else case.page_size
+    cen_tol = (nmax + 1) * 2.0 ** -24 * kabs
+    for b in range(case.batch):
+        nb = int(n[b])
+        assert np.array_equal(wide(kmin)[b, :, :nb], omin[b, :, :nb]), "kmin not bit-exact"
+        assert np.array_equal(wide(kmax)[b, :, :nb], omax[b, :, :nb]), "kmax not bit-exact"
+        assert np.max(np.abs(cen[b, :, :nb] - ocen[b, :, :nb])) <= cen_tol
+    # 2. scores within 1e-4 D
+    _, osc, oden = oracle.score_decode(case.q, oc, (omin, omax, ocen), kind, case.chunk_starts, case.num_chunks)
+    worst = check_scores(scores, osc, oden, n, case.name)
+    # 3a. selection is an exact function of the scores it is given
+    rsel, rcnt = oracle_select(scores.astype(np.float64), case, budget)
+    assert np.array_equal(cnt, rcnt), "selection count differs from the oracle on identical scores"
+    for b in range(case.batch):
+        for h in range(case.num_kv_heads):
+            assert np.array_equal(sel[b, h, :cnt[b, h]], rsel[b, h, :rcnt[b, h]]), (b, h)
+            assert np.all(sel[b, h, cnt[b, h]:] == -1)
+    # 3b. against the oracle's own scores: band rule
+    osel, ocnt = oracle_select(osc, case, budget)
+    diffs = check_band(sel, cnt, osel, ocnt, osc, oden, n, forced, exact_count=band_exact_count)
+    # 4. attention on the GPU's selection
+    ref = oracle.decode_attn(case.q, oc, sel, cnt, chunk_starts=case.chunk_starts, num_chunks=case.num_chunks)
+    tol = ATTN_ABS[case.dtype]
+    for s, out in outs.items():
+        err = max_abs(_np(out), ref)
+        assert err <= tol, f"splits={s}: attention max-abs {err:.3g} > {tol}"
+    if check_dense:
+        dref = oracle.decode_attn(case.q, oc, chunk_starts=case.chunk_starts, num_chunks=case.num_chunks)
+        derr = max_abs(_np(dense), dref)
+        assert derr <= tol, f"dense max-abs {derr:.3g}"
+    log(f"  ok: worst score err {worst:.2e} D, in-band selection diffs {diffs}, attn err "
+        f"{max(max_abs(_np(o), ref) for o in outs.values()):.2e}")
+    return {"sel": sel, "cnt": cnt, "out": _np(next(iter(outs.values()))), "ref": ref, "osel": osel, "ocnt": ocnt}
+
+
+def test_tiny_fp32_decode(dev):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.tiny_decode()
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.topk(8), splits=(0, 1, 3, 8))
+    assert np.all(r["cnt"] == 8)
+
+
+@pytest.mark.parametrize("kind", ["envelope", "centroid"])
+@pytest.mark.parametrize("k", [256, 512])
+def test_replay_decode(dev, kind, k):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.replay_decode()
+    kd = ops.BSA_ENVELOPE if kind == "envelope" else ops.BSA_CENTROID
+    r = run_decode_case(case, dev, kd, ops.Budget.topk(k), splits=(0, 1, 7))
+    assert np.all(r["cnt"] == k)
+    # the planted needle pages are found
+    needles = set(case.info["needle_pages"].tolist())
+    for h in range(case.num_kv_heads):
+        assert needles <= set(r["sel"][0, h, :k].tolist())
+
+
+@pytest.mark.parametrize("tokens", [4096, 8192, 16384, 1 << 20])
+def test_varchunk_decode(dev, tokens):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.varchunk_decode()
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.token_budget(tokens), band_exact_count=False,
+                        check_dense=tokens == 4096)
+    lens = case.chunk_len[0]
+    for h in range(case.num_kv_heads):
+        tot = int(lens[r["sel"][0, h, :r["cnt"][0, h]]].sum())
+        assert tot <= tokens and (tot > tokens - 256 or tot == int(case.seq_lens[0]))
+    if tokens >= int(case.seq_lens[0]):
+        dense = oracle.decode_attn(case.q, oracle_cache(case), chunk_starts=case.chunk_starts,
+                                   num_chunks=case.num_chunks)
+        assert max_abs(r["out"], dense) <= ATTN_ABS["bf16"]
+
+
+def test_varchunk_16k_budget_is_dense(dev):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.varchunk_decode(cid=2, seq_len=16384)
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.token_budget(16384), band_exact_count=False,
+                        check_dense=False)
+    assert np.all(r["cnt"][0] == case.num_chunks[0])
+    dense = oracle.decode_attn(case.q, oracle_cache(case), chunk_starts=case.chunk_starts, num_chunks=case.num_chunks)
+    assert max_abs(r["out"], dense) <= ATTN_ABS["bf16"]
+
+
+@pytest.mark.parametrize("ratio", synth.RATIOS)
+@pytest.mark.parametrize("kind", ["centroid", "envelope"])
+def test_batched_ratio_small(dev, ratio, kind):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.batched_decode(cid=13, batch=5, lo=700, hi=3000)
+    bos = 1 if kind == "centroid" else 0
+    kd = ops.BSA_CENTROID if kind == "centroid" else ops.BSA_ENVELOPE
+    forced = (("bos",) if bos else ()) + ("eos",)
+    r = run_decode_case(case, dev, kd, ops.Budget.ratio_budget(ratio, bos, 1), forced=forced,
+                        check_dense=ratio == 0.5)
+    n = case.n_chunks()
+    for b in range(case.batch):
+        K = min(int(n[b]), max(2 + bos, int(math.floor(int(n[b]) * ratio))))
+        for h in range(case.num_kv_heads):
+            s = r["sel"][b, h, :r["cnt"][b, h]]
+            assert r["cnt"][b, h] == K
+            assert int(n[b]) - 1 in s and (not bos or 0 in s)
+
+
+def test_nan_tail_slots_are_never_read(dev):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(21, batch=3, seq_lens=[33, 250, 1001], num_q_heads=16, num_kv_heads=2, head_dim=128,
+                             pad_value=float("nan"), name="nan-tail")
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.topk(5), splits=(0, 1, 2))
+    assert np.all(np.isfinite(r["out"]))
+
+
+@pytest.mark.parametrize("g", [1, 3, 12, 16])
+def test_group_sizes_and_head_dim_64(dev, g):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(30 + g, batch=2, seq_lens=[517, 1200], num_q_heads=2 * g, num_kv_heads=2, head_dim=64,
+                             name=f"g{g}-d64")
+    run_decode_case(case, dev, ops.BSA_CENTROID, ops.Budget.topk(12), splits=(0, 1, 5))
+
+
+def test_page_size_32_uses_general_path(dev):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(40, batch=2, seq_lens=[300, 1000], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                             page_size=32, name="page32")
+    run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.topk(6), splits=(0, 3))
+
+
+def test_deterministic_bits(dev):
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.batched_decode(cid=14, batch=4, lo=2000, hi=5000)
+    kv, _ = gpu_kv(case, dev)
+    q = ops.upload(case.q, dev)
+    outs = []
+    for _ in range(2):
+        meta = ops.build_chunk_meta(kv)
+        sc = ops.score_chunks(q, kv, meta, ops.BSA_ENVELOPE)
+        sel, cnt = ops.select_topk(sc, kv, ops.Budget.ratio_budget(0.125, 0, 1))
+        outs.append(ops.sparse_attn_decode(q, kv, sel, cnt).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("ratio", [0.5, 0.125])
+def test_batched_ratio_full_size(dev, ratio):
+    """16 sequences with lengths in [8192, 32768], 64 q / 8 KV heads (the
+    benchmark's batched workload) at two ratios, centroid with bos+eos."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.batched_decode()
+    run_decode_case(case, dev, ops.BSA_CENTROID, ops.Budget.ratio_budget(ratio, 1, 1), forced=("bos", "eos"),
+                    check_dense=ratio == 0.125)
