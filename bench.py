@@ -1,16 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark: sparse decode tokens/s and effective HBM bandwidth on one MI355X.
 
-Workload (default): one decode layer shaped like the replay study's model
+Headline workload: one decode layer shaped like the replay study's model
 (32 q / 4 KV heads, head_dim 128, bf16, 16-token pages) at 29,504 cached tokens
-with a 4096-token budget (top 256 pages), envelope scoring.  One step = chunk
-scoring + per-KV-head top-k + split-K sparse attention + merge for the whole
-batch; chunk metadata is built once before timing (it is amortised over 16
-decode steps per page in a live loop) and its build time is reported apart.
-Inputs are synthetic (seeded, see block_sparse_attention_chunk_amd/synth.py)
-and resident in HBM before the timed region.  To keep the 256 MB last-level
-cache from serving the reads, steps rotate over replicas of the cache and
-metadata whose total exceeds 1 GiB.
+with a 4096-token budget (top 256 of 1,844 pages), envelope scoring, one
+sequence.  One step = chunk scoring + per-KV-head top-k + split-K sparse
+attention (merge included) for the whole batch.  Chunk metadata is built once
+before timing (in a live loop a page's metadata is written once per 16 decode
+steps) and its build time is reported apart.
+
+Inputs are synthetic and seeded (block_sparse_attention_chunk_amd/synth.py)
+and resident in HBM before the timed region.  Steps rotate over replicas of
+the cache and metadata whose total exceeds 1 GiB, so the 256 MB last-level
+cache cannot serve the reads.  Each step is captured once in a HIP graph and
+replayed, so host dispatch is not in the measurement.
+
+Extra records in the same JSON line: the same layer with 16 sequences at
+32,768 tokens; a 64 q / 8 KV-head batch of 16 x 32,768 tokens at ratio 1/8
+(4096 tokens per sequence and head); the 131,072-token router prefill (28 q /
+4 KV heads, k = 32, rho = 2) with its MFMA utilisation; with --extra also the
+seven ratios of the 8K-32K batched workload, both scorings.
 
 Prints one JSON line.  --gpus N > 1 is refused (one GPU per box).
 """
@@ -30,6 +39,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -39,98 +49,281 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--budget", type=int, default=4096, help="attended tokens per (sequence, KV head)")
     ap.add_argument("--scoring", choices=["envelope", "centroid"], default="envelope")
-    ap.add_argument("--batch", type=int, default=1)
-    ap.add_argument("--seq-len", type=int, default=29504)
-    ap.add_argument("--replicas-gib", type=float, default=1.0, help="rotate replicas until this much is touched")
+    ap.add_argument("--replicas-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--extra", action="store_true", help="also time the batched and prefill workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched extra records")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the router prefill record")
+    ap.add_argument("--extra", action="store_true", help="also the seven-ratio batched sweep")
+    ap.add_argument("--only-headline-kernel", action="store_true",
+                    help="profiling aid: time only the headline workload")
     return ap.parse_args()
 
 
-class Step:
-    """Device buffers and the hot path of one decode step."""
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    def __init__(self, case, budget_tokens, scoring, replicas, dev):
+
+class DecodeBench:
+    """Device buffers, graphs and timings of one decode workload."""
+
+    def __init__(self, case, budget, scoring, dev, replicas_gib=1.0):
         import torch
         from block_sparse_attention_chunk_amd import ops
-        self.ops, self.torch = ops, torch
-        self.case = case
+        self.ops, self.torch, self.case, self.dev = ops, torch, case, dev
+        self.scoring = scoring
         self.kind = ops.BSA_ENVELOPE if scoring == "envelope" else ops.BSA_CENTROID
-        self.k_pages = budget_tokens // case.page_size
-        self.budget = ops.Budget.topk(self.k_pages)
+        self.budget = budget
         base_k, base_v = ops.upload(case.k, dev), ops.upload(case.v, dev)
         self.q = ops.upload(case.q, dev)
         bt, sl = ops.upload(case.block_table, dev), ops.upload(case.seq_lens, dev)
-        which = ops.BSA_META_ENVELOPE if self.kind == ops.BSA_ENVELOPE else ops.BSA_META_CENTROID
+        self.which = ops.BSA_META_ENVELOPE if self.kind == ops.BSA_ENVELOPE else ops.BSA_META_CENTROID
+        kv_bytes = case.k.nbytes + case.v.nbytes
+        self.replicas = max(1, math.ceil(replicas_gib * 2 ** 30 / kv_bytes))
         self.reps = []
-        for r in range(replicas):
+        for r in range(self.replicas):
             k = base_k if r == 0 else base_k.clone()
             v = base_v if r == 0 else base_v.clone()
             kv = ops.KVCache(k, v, sl, case.page_size, bt)
-            meta = ops.build_chunk_meta(kv, which=which)
-            self.reps.append((kv, meta))
+            self.reps.append((kv, ops.build_chunk_meta(kv, which=self.which)))
         kv0 = self.reps[0][0]
-        self.max_sel = self.budget.max_selected(kv0.max_pages)
-        self.scores = torch.empty((case.batch, case.num_kv_heads, kv0.max_pages), dtype=torch.float32, device=dev)
-        self.sel = torch.empty((case.batch, case.num_kv_heads, self.max_sel), dtype=torch.int32, device=dev)
-        self.cnt = torch.empty((case.batch, case.num_kv_heads), dtype=torch.int32, device=dev)
-        self.out = torch.empty((case.batch, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
-        need = ops.decode_workspace_bytes(kv0, case.num_q_heads, self.max_sel)
-        self.ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        self.max_sel = budget.max_selected(kv0.max_pages)
+        B, H = case.batch, case.num_kv_heads
+        self.scores = torch.empty((B, H, kv0.max_pages), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, H, self.max_sel), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
+        self.ws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, self.max_sel), 1),),
+                              dtype=torch.uint8, device=dev)
+        self.dws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, kv0.max_pages), 1),),
+                               dtype=torch.uint8, device=dev)
         self.splits = ops.decode_num_splits(kv0, case.num_q_heads, self.max_sel)
-        self.meta_which = which
+        self.dense_splits = ops.decode_num_splits(kv0, case.num_q_heads, kv0.max_pages)
 
-    def run(self, i, ev=None):
+    # --- the hot path ---------------------------------------------------------------
+    def select(self, r):
         ops = self.ops
-        kv, meta = self.reps[i % len(self.reps)]
+        kv, meta = self.reps[r]
         ops.score_chunks(self.q, kv, meta, self.kind, out=self.scores)
         ops.select_topk(self.scores, kv, self.budget, max_sel=self.max_sel, sel_idx=self.sel, sel_count=self.cnt)
-        if ev is not None:
-            ev[0].record()
-        ops.sparse_attn_decode(self.q, kv, self.sel, self.cnt, out=self.out, workspace=self.ws)
-        if ev is not None:
-            ev[1].record()
 
-    def dense(self, i):
-        kv, _ = self.reps[i % len(self.reps)]
-        self.ops.sparse_attn_decode(self.q, kv, None, None, out=self.out, workspace=self._dense_ws(kv))
+    def attend(self, r):
+        kv, _ = self.reps[r]
+        self.ops.sparse_attn_decode(self.q, kv, self.sel, self.cnt, out=self.out, workspace=self.ws)
 
-    def _dense_ws(self, kv):
-        if not hasattr(self, "_dws"):
-            need = self.ops.decode_workspace_bytes(kv, self.case.num_q_heads, kv.max_pages)
-            self._dws = self.torch.empty((max(need, 1),), dtype=self.torch.uint8, device=self.q.device)
-        return self._dws
+    def step(self, r):
+        self.select(r)
+        self.attend(r)
+
+    def dense(self, r):
+        kv, _ = self.reps[r]
+        self.ops.sparse_attn_decode(self.q, kv, None, None, out=self.out, workspace=self.dws)
+
+    def meta(self, r):
+        kv, meta = self.reps[r]
+        self.ops.build_chunk_meta(kv, which=self.which, meta=meta)
+
+    # --- graphs and timing ----------------------------------------------------------
+    def graph(self, fn, reps):
+        torch = self.torch
+        for r in reps:   # code objects are loaded before capture
+            fn(r)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in reps:
+                fn(r)
+        torch.cuda.synchronize()
+        return g
+
+    def time_steps(self, steps, warmup):
+        """Exactly `steps` decode steps, rotating replicas, from HIP graphs."""
+        torch = self.torch
+        R = self.replicas
+        g_all = self.graph(self.step, range(R))
+        g_one = [self.graph(self.step, [r]) for r in range(R)]
+
+        def run(n, start):
+            full, rem = divmod(n, R)
+            for _ in range(full):
+                g_all.replay()
+            for r in range(rem):
+                g_one[(start + r) % R].replay()
+
+        run(warmup, 0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(steps, 0)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def time_kernel(self, fn, min_launches=200):
+        """Average duration of one launch of fn: back-to-back launches over all
+        replicas in one graph, bracketed by HIP events on the launch stream."""
+        torch = self.torch
+        R = self.replicas
+        per = max(1, math.ceil(min_launches / R))
+        g = self.graph(fn, list(range(R)) * 1)
+        stream = torch.cuda.current_stream(self.dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        e0.record(stream)
+        for _ in range(per):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (per * R)
+
+    def bytes(self):
+        """Algorithmic bytes of one step: metadata read + selected K/V + q in + out."""
+        case = self.case
+        D, H, Hq, B, P = case.head_dim, case.num_kv_heads, case.num_q_heads, case.batch, case.page_size
+        n = case.n_chunks()
+        meta_per_chunk = 2 * D * 2 if self.scoring == "envelope" else D * 4
+        meta = int(n.sum()) * H * meta_per_chunk
+        sel_tokens = 0
+        for b in range(B):
+            L = int(case.seq_lens[b])
+            K = self.budget.max_selected(int(n[b]))      # pages kept per head
+            full = min(K, int(n[b]))
+            tokens = full * P if full < int(n[b]) else L  # all pages: the partial last page counts its tokens
+            sel_tokens += min(tokens, L)
+        kvb = sel_tokens * H * D * 2 * 2
+        dense_kv = int(case.seq_lens.sum()) * H * D * 2 * 2
+        qo = B * Hq * D * (2 + 4)
+        return meta, kvb, qo, dense_kv
+
+    def measure(self, steps, warmup):
+        t_step = self.time_steps(steps, warmup)
+        self.step(0)
+        t_attn = self.time_kernel(self.attend)
+        t_dense = self.time_kernel(self.dense)
+        t_sel = self.time_kernel(self.select)
+        t_meta = self.time_kernel(self.meta)
+        meta_b, kv_b, qo_b, dense_b = self.bytes()
+        return {"t_step": t_step, "t_attn": t_attn, "t_dense": t_dense, "t_select": t_sel, "t_meta": t_meta,
+                "meta_bytes": meta_b, "kv_bytes": kv_b, "qo_bytes": qo_b, "dense_kv_bytes": dense_b}
 
 
-def bytes_per_step(case, k_pages, scoring):
-    """Algorithmic bytes of one step: metadata read + selected K/V + q in + out."""
-    D, H, Hq, B = case.head_dim, case.num_kv_heads, case.num_q_heads, case.batch
-    n_pages = int(np.sum((case.seq_lens + case.page_size - 1) // case.page_size))
-    meta_per_chunk = 2 * D * 2 if scoring == "envelope" else D * 4
-    meta = n_pages * H * meta_per_chunk
-    sel_tokens = 0
-    for b in range(B):
-        L = int(case.seq_lens[b])
-        sel_tokens += min(k_pages * case.page_size, L)
-    kvb = sel_tokens * H * D * 2 * 2
-    qo = B * Hq * D * (2 + 4)
-    return meta, kvb, qo
+def record(name, bench, m):
+    case = bench.case
+    step_bytes = m["meta_bytes"] + m["kv_bytes"] + m["qo_bytes"]
+    return {
+        "workload": name,
+        "batch": case.batch, "seq_len": int(case.seq_lens.max()), "q_heads": case.num_q_heads,
+        "kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "scoring": bench.scoring,
+        "tokens_per_s": case.batch / m["t_step"],
+        "us_per_step": m["t_step"] * 1e6,
+        "effective_hbm_gbs": step_bytes / m["t_step"] / 1e9,
+        "effective_hbm_frac": step_bytes / m["t_step"] / 1e9 / HBM_PEAK_GBS,
+        "sparse_attn_us": m["t_attn"] * 1e6,
+        "selected_kv_gbs": m["kv_bytes"] / m["t_attn"] / 1e9,
+        "selected_kv_frac": m["kv_bytes"] / m["t_attn"] / 1e9 / HBM_PEAK_GBS,
+        "score_select_us": m["t_select"] * 1e6,
+        "meta_build_us": m["t_meta"] * 1e6,
+        "dense_attn_us": m["t_dense"] * 1e6,
+        "dense_kv_gbs": m["dense_kv_bytes"] / m["t_dense"] / 1e9,
+        "speedup_attn_vs_dense": m["t_dense"] / m["t_attn"],
+        "speedup_step_vs_dense": m["t_dense"] / m["t_step"],
+        "splits": bench.splits,
+        "cache_replicas": bench.replicas,
+        "bytes_per_step": {"metadata": m["meta_bytes"], "selected_kv": m["kv_bytes"], "q_out": m["qo_bytes"]},
+    }
 
 
-def time_loop(fn, steps, warmup, torch):
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        fn(warmup + i)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+class PrefillBench:
+    """Router prefill over query tiles: block metadata, tile scores, the
+    uncertainty router and the sparse / dense causal tile attention."""
+
+    def __init__(self, pc, dev, kind, k=32, rho=2, quantile=0.25):
+        import torch
+        from block_sparse_attention_chunk_amd import ops
+        self.ops, self.torch, self.pc, self.dev = ops, torch, pc, dev
+        self.kind, self.k, self.rho, self.quantile = kind, k, rho, quantile
+        self.kv = ops.KVCache(ops.upload(pc.k, dev), ops.upload(pc.v, dev),
+                              torch.tensor([pc.T], dtype=torch.int32, device=dev), pc.block, token_major=True)
+        self.q = ops.upload(pc.q, dev)
+        which = ops.BSA_META_ENVELOPE if kind == ops.BSA_ENVELOPE else ops.BSA_META_CENTROID
+        self.which = which
+        self.meta = ops.build_chunk_meta(self.kv, which=which)
+        nt = (pc.T + pc.tile - 1) // pc.tile
+        self.n_tiles = nt
+        self.ts = torch.empty((nt, pc.num_kv_heads, self.kv.max_pages), dtype=torch.float32, device=dev)
+        self.ws = torch.empty((max(ops.router_workspace_bytes(nt, pc.num_kv_heads, k, rho), 1),), dtype=torch.uint8,
+                              device=dev)
+        self.out = torch.empty((pc.T, pc.num_q_heads, pc.head_dim), dtype=torch.float32, device=dev)
+        self.r = None
+
+    def build_meta(self, _=0):
+        self.ops.build_chunk_meta(self.kv, which=self.which, meta=self.meta)
+
+    def score(self, _=0):
+        self.ops.score_chunks(self.q, self.kv, self.meta, self.kind, rows_per_query=self.pc.tile, causal=True,
+                              out=self.ts)
+
+    def route(self, _=0):
+        self.r = self.ops.select_topk_router(self.ts, k=self.k, rho=self.rho, quantile=self.quantile,
+                                             workspace=self.ws)
+
+    def attend(self, _=0):
+        self.ops.sparse_attn_tile_prefill(self.q, self.kv, self.r["kv_idx"], out=self.out)
+
+    def dense(self, _=0):
+        self.ops.sparse_attn_tile_prefill(self.q, self.kv, None, out=self.out)
+
+    def timed(self, fn, reps):
+        torch = self.torch
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    def measure(self, reps=5):
+        t_meta = self.timed(self.build_meta, reps)
+        t_score = self.timed(self.score, reps)
+        t_route = self.timed(self.route, reps)
+        t_attn = self.timed(self.attend, reps)
+        t_dense = self.timed(self.dense, max(1, reps // 2))
+        pc = self.pc
+        g = pc.num_q_heads // pc.num_kv_heads
+        kv_idx = self.r["kv_idx"].cpu().numpy()
+        n_sel = int((kv_idx >= 0).sum())                        # (tile, KV head, block) triples attended
+        trig = int(self.r["triggered"].sum().item())
+        R, Bk, D = pc.tile, pc.block, pc.head_dim
+        attn_flops = 4.0 * R * Bk * D * g * n_sel               # QK^T + PV, full blocks
+        nt = self.n_tiles
+        vis_pairs = sum(min(t + 1, self.kv.max_pages) for t in range(nt)) * pc.num_kv_heads
+        score_flops = 2.0 * R * g * (2 * D) * vis_pairs        # [q+|q-] x [kmax;kmin] per visible block
+        dense_flops = 4.0 * R * Bk * D * g * vis_pairs
+        t_sparse = t_score + t_route + t_attn
+        peak = BF16_MFMA_PEAK_TFLOPS * 1e12
+        return {
+            "workload": f"router prefill, {pc.T} tokens, {pc.num_q_heads} q / {pc.num_kv_heads} KV heads, d {D}, "
+                        f"bf16, 64-token blocks / 64-row tiles, k={self.k}, rho={self.rho}, quantile "
+                        f"{self.quantile}, {'envelope' if self.kind == 0 else 'centroid'} scoring",
+            "tokens_per_s": pc.T / t_sparse,
+            "sparse_pipeline_ms": t_sparse * 1e3,
+            "meta_build_ms": t_meta * 1e3, "tile_score_ms": t_score * 1e3, "router_ms": t_route * 1e3,
+            "sparse_attn_ms": t_attn * 1e3, "dense_causal_attn_ms": t_dense * 1e3,
+            "sparse_pipeline_vs_dense_attn": t_sparse / t_dense,
+            "triggered_tiles": trig, "attended_blocks": n_sel,
+            "attn_tflops": attn_flops / t_attn / 1e12, "attn_mfma_frac": attn_flops / t_attn / peak,
+            "score_tflops": score_flops / t_score / 1e12, "score_mfma_frac": score_flops / t_score / peak,
+            "dense_tflops": dense_flops / t_dense / 1e12, "dense_mfma_frac": dense_flops / t_dense / peak,
+            "roofline": {"bound": "mfma", "kernel": "tile_prefill_kernel", "achieved": attn_flops / t_attn / 1e12,
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": attn_flops / t_attn / peak,
+                         "traffic": None},
+        }
 
 
 def cpu_baseline(case, k_pages, scoring, seconds):
-    """The fp64 oracle on the host cores, same inputs and stages (score + select + attention)."""
+    """The fp64 oracle on the host cores on the same inputs and stages (score +
+    select + attention per step, metadata built once), run for ~`seconds`."""
     import oracle
     oc = oracle.PagedCache(case.k, case.v, case.block_table, case.seq_lens, case.page_size, case.num_kv_heads,
                            case.head_dim)
@@ -148,86 +341,95 @@ def cpu_baseline(case, k_pages, scoring, seconds):
             break
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": case.batch * steps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} full decode steps of the benchmarked workload (score + select + attention) in "
-                      f"{el:.1f} s, fp64, OpenMP {threads} threads"}
+            "sample": f"{steps} complete decode steps of the headline workload (score + select + attention over "
+                      f"the same inputs; metadata built once) in {el:.1f} s, fp64, OpenMP {threads} threads"}
 
 
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path exists)"}))
         sys.exit(2)
     import torch
     from block_sparse_attention_chunk_amd import ops, synth
     dev = torch.device("cuda:0")
-    if a.batch == 1:
-        case = synth.replay_decode(seq_len=a.seq_len)
-    else:
-        case = synth.replay_decode(seq_len=a.seq_len, batch=a.batch)
+
+    log("headline: replay-shaped decode layer")
+    case = synth.replay_decode()
     k_pages = a.budget // case.page_size
-    kv_bytes = (case.k.nbytes + case.v.nbytes)
-    replicas = max(1, math.ceil(a.replicas_gib * 2 ** 30 / kv_bytes))
-    st = Step(case, a.budget, a.scoring, replicas, dev)
-    torch.cuda.synchronize()
-
-    # metadata build, timed apart
-    kv0 = st.reps[0][0]
-    t_meta = time_loop(lambda i: ops.build_chunk_meta(st.reps[i % replicas][0], which=st.meta_which,
-                                                      meta=st.reps[i % replicas][1]), 20, 3, torch)
-
-    # the timed region: K full steps
-    stream = torch.cuda.current_stream(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for i in range(a.warmup):
-        st.run(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        st.run(a.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / a.steps
-    t_attn = float(np.mean([s.elapsed_time(e) for s, e in evs])) * 1e-3
-    t_dense = time_loop(st.dense, max(20, a.steps // 4), 5, torch)
-
-    meta_b, kv_b, qo_b = bytes_per_step(case, k_pages, a.scoring)
-    step_bytes = meta_b + kv_b + qo_b
-    tok_s = case.batch / t_step
-    eff_gbs = step_bytes / t_step / 1e9
-    attn_gbs = kv_b / t_attn / 1e9
-    n_pages = int(np.sum((case.seq_lens + 15) // 16))
-    dense_kv = int(np.sum(case.seq_lens)) * case.num_kv_heads * case.head_dim * 4
+    hb = DecodeBench(case, ops.Budget.topk(k_pages), a.scoring, dev, a.replicas_gib)
+    m = hb.measure(a.steps, a.warmup)
+    head = record(f"replay-shaped decode, {case.num_q_heads} q / {case.num_kv_heads} KV heads, d 128, bf16, "
+                  f"{int(case.seq_lens[0])} tokens, {a.scoring} scoring, top-{k_pages} of "
+                  f"{int(case.n_chunks()[0])} 16-token pages (budget {k_pages * 16} tokens), 1 sequence", hb, m)
     res = {
         "metric": "sparse decode tokens/s + effective HBM GB/s (% of peak) at 32K ctx, budget 4096",
-        "value": tok_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": t_step * 1e3,
+        "ms_per_step": m["t_step"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) keys/values, planted needle pages, 4 outlier channels x8)",
-        "config": {"workload": f"replay-shaped decode layer, {a.scoring} scoring, top-{k_pages} pages "
-                               f"(budget {k_pages * 16} tokens) of {n_pages} 16-token pages",
-                   "batch": case.batch, "seq_len": int(case.seq_lens[0]), "q_heads": case.num_q_heads,
-                   "kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "page_size": case.page_size,
-                   "budget_tokens": a.budget, "scoring": a.scoring, "splits": st.splits,
-                   "cache_replicas": replicas},
-        "effective_hbm_gbs": eff_gbs,
-        "effective_hbm_frac": eff_gbs / HBM_PEAK_GBS,
-        "bytes_per_step": {"metadata": meta_b, "selected_kv": kv_b, "q_out": qo_b},
-        "meta_build_us": t_meta * 1e6,
-        "dense_decode_us": t_dense * 1e6,
-        "sparse_attn_us": t_attn * 1e6,
-        "speedup_vs_dense_attention": t_dense / t_attn,
-        "speedup_vs_dense_step": t_dense / t_step,
-        "roofline": {"bound": "hbm", "kernel": "bsa_sparse_attn_decode (split-K kernel + merge)",
-                     "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
-                     "traffic": None},
+        "data": "synthetic: seeded N(0,1) keys/values, 24 planted needle pages, 4 outlier channels x8",
+        "config": {"workload": head["workload"], "batch": 1, "seq_len": int(case.seq_lens[0]),
+                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+                   "page_size": case.page_size, "budget_tokens": k_pages * 16, "scoring": a.scoring,
+                   "splits": hb.splits, "cache_replicas": hb.replicas, "graph_replay": True},
+        "effective_hbm_gbs": head["effective_hbm_gbs"],
+        "effective_hbm_frac": head["effective_hbm_frac"],
+        "roofline": {"bound": "hbm", "kernel": "decode_paged16_kernel (bsa_sparse_attn_decode, merge fused)",
+                     "achieved": head["selected_kv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["selected_kv_frac"], "traffic": None},
+        "headline": head,
     }
+    del hb
+    torch.cuda.empty_cache()
+
+    if not a.no_batched and not a.only_headline_kernel:
+        extra = []
+        log("batched: replay-shaped layer, 16 sequences x 32768 tokens")
+        c16 = synth.replay_decode(seq_len=32768, batch=16)
+        b16 = DecodeBench(c16, ops.Budget.topk(256), "envelope", dev, a.replicas_gib)
+        extra.append(record("replay-shaped decode, 16 x 32768 tokens, envelope, top-256 pages (4096 tokens)", b16,
+                            b16.measure(max(50, a.steps // 4), 5)))
+        del b16, c16
+        torch.cuda.empty_cache()
+        log("batched: 64 q / 8 KV heads, 16 x 32768 tokens, ratio 1/8")
+        c3 = synth.batched_decode(cid=3, seq_lens=[32768] * 16)
+        b3 = DecodeBench(c3, ops.Budget.ratio_budget(0.125, 1, 1), "centroid", dev, a.replicas_gib)
+        extra.append(record("batched decode, 64 q / 8 KV heads, 16 x 32768 tokens, centroid, ratio 1/8 with "
+                            "bos+eos (4096 tokens per sequence and head)", b3, b3.measure(max(50, a.steps // 4), 5)))
+        del b3, c3
+        torch.cuda.empty_cache()
+        res["batched"] = extra
+    if not a.no_prefill and not a.only_headline_kernel:
+        log("router prefill: 131072 tokens")
+        pc = synth.router_prefill()
+        pb = PrefillBench(pc, dev, ops.BSA_ENVELOPE)
+        res["prefill"] = pb.measure()
+        del pb, pc
+        torch.cuda.empty_cache()
+    if a.extra:
+        log("ratio sweep: 16 sequences of 8K-32K tokens, 64 q / 8 KV heads")
+        c3 = synth.batched_decode()
+        sweep = []
+        for scoring, bos in (("centroid", 1), ("envelope", 0)):
+            for ratio in synth.RATIOS:
+                b3 = DecodeBench(c3, ops.Budget.ratio_budget(ratio, bos, 1), scoring, dev, a.replicas_gib)
+                rec = record(f"batched decode, ratio {ratio}, {scoring}", b3, b3.measure(40, 5))
+                sweep.append({k: rec[k] for k in ("workload", "tokens_per_s", "us_per_step", "sparse_attn_us",
+                                                  "selected_kv_gbs", "selected_kv_frac", "dense_attn_us",
+                                                  "speedup_attn_vs_dense", "speedup_step_vs_dense",
+                                                  "effective_hbm_gbs")})
+                del b3
+                torch.cuda.empty_cache()
+        res["ratio_sweep"] = sweep
     if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(case, k_pages, a.scoring, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 

@@ -101,11 +101,11 @@ constexpr int kMaxRouterTiles = 8192;
 int resolve_splits(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
     if (num_splits > 0) return num_splits;
     const int bh = kv->batch * kv->num_kv_heads;
-    int s = (2048 + bh - 1) / bh;                       // aim at ~2048 workgroups (8 per CU)
+    int s = (512 + bh - 1) / bh;                        // aim at ~512 workgroups (2 per CU, 3 resident)
     const int cap = (max_items + 7) / 8;                // at least ~8 items per workgroup
     if (s > cap) s = cap;
     if (s < 1) s = 1;
-    if (s > 256) s = 256;
+    if (s > 64) s = 64;
     return s;
 }
 
@@ -260,6 +260,7 @@ int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max
 size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits) {
     const int s = bsa_decode_num_splits(kv, num_q_heads, max_items, num_splits);
     if (s <= 1 || !kv) return 0;
+    // partial outputs and (max, sum) pairs of every split
     return (size_t)kv->batch * num_q_heads * s * (kv->head_dim + 2) * sizeof(float);
 }
 

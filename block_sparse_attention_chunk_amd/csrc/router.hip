@@ -16,8 +16,7 @@
 // between order statistics; strict '<'; sentinel -1 after ascending ids.
 //
 // Three launches: (1) one workgroup per (tile, KV head) selects the top
-// max(rho*k, k+1) blocks with the weighted radix select of select.hip's
-// scheme, sorts them (bitonic in LDS) and writes sigma plus the score-ordered
+// max(rho*k, k+1) blocks with the radix select of radix_select.h, sorts them (bitonic in LDS) and writes sigma plus the score-ordered
 // list; (2) one workgroup computes sigma_bar, the threshold and the trigger
 // flags (the path's only device-wide dependency); (3) one workgroup per
 // (tile, KV head) emits the ascending, sentinel-padded kv_idx row.
@@ -54,14 +53,14 @@ __device__ void bitonic_desc_u64(uint64_t *v, int n2) {
     }
 }
 
-__global__ __launch_bounds__(kRtThreads) void router_topk_kernel(const float *__restrict__ ts, int n_blocks,
-                                                                 int hkv, int causal, int k, int rho,
-                                                                 float *__restrict__ sigma,
-                                                                 int32_t *__restrict__ top) {
-    extern __shared__ uint32_t keys[];
-    __shared__ int hist[256];
-    __shared__ int scan[8];
-    __shared__ int bcast[2];
+constexpr int kRtPer = 8;   // candidates per thread: up to 8 * NT blocks per tile
+
+template <int NT>
+__global__ __launch_bounds__(NT) void router_topk_kernel(const float *__restrict__ ts, int n_blocks, int hkv,
+                                                            int causal, int k, int rho, float *__restrict__ sigma,
+                                                            int32_t *__restrict__ top) {
+    __shared__ RadixShared sh;
+    __shared__ uint32_t skeys[NT * kRtPer];
     __shared__ int sel[kMaxList];
     __shared__ uint64_t list[kMaxList];
     const int t = blockIdx.x, h = blockIdx.y;
@@ -69,18 +68,25 @@ __global__ __launch_bounds__(kRtThreads) void router_topk_kernel(const float *__
     const int width = rho * k;
     const int want = min(max(width, k + 1), n);
     const float *row = ts + ((int64_t)t * hkv + h) * n_blocks;
-    for (int i = threadIdx.x; i < n; i += kRtThreads) keys[i] = float_key(row[i]);
+    const int base = threadIdx.x * kRtPer;
+    uint32_t keys[kRtPer];
+    int wts[kRtPer];
+#pragma unroll
+    for (int i = 0; i < kRtPer; ++i) {
+        keys[i] = base + i < n ? float_key(row[base + i]) : 0u;
+        wts[i] = 1;
+        if (base + i < n) skeys[base + i] = keys[i];
+    }
+    const int cnt = radix_select_prefix<NT, kRtPer>(keys, wts, base, n, want, sel, kMaxList, sh);
     __syncthreads();
-    auto unit = [](int) { return 1; };
-    const int cnt = radix_select_prefix(keys, n, want, unit, sel, kMaxList, hist, scan, bcast);
     int n2 = 1;
     while (n2 < cnt) n2 <<= 1;
-    for (int i = threadIdx.x; i < n2; i += kRtThreads)
-        list[i] = i < cnt ? ((uint64_t)keys[sel[i]] << 32) | (uint64_t)(0xffffffffu - (uint32_t)sel[i]) : 0ull;
+    for (int i = threadIdx.x; i < n2; i += NT)
+        list[i] = i < cnt ? ((uint64_t)skeys[sel[i]] << 32) | (uint64_t)(0xffffffffu - (uint32_t)sel[i]) : 0ull;
     __syncthreads();
     bitonic_desc_u64(list, n2);
     int32_t *dst = top + ((int64_t)t * hkv + h) * width;
-    for (int i = threadIdx.x; i < width; i += kRtThreads)
+    for (int i = threadIdx.x; i < width; i += NT)
         dst[i] = i < min(cnt, width) ? (int32_t)(0xffffffffu - (uint32_t)(list[i] & 0xffffffffu)) : -1;
     if (threadIdx.x == 0) {
         double sg = 1.0;
@@ -208,8 +214,12 @@ hipError_t launch_router(const float *ts, int32_t n_tiles, int32_t hkv, int32_t 
                          uint8_t *triggered, float *threshold, void *ws, hipStream_t s) {
     int32_t *top = (int32_t *)ws;
     dim3 grid(n_tiles, hkv);
-    hipLaunchKernelGGL(router_topk_kernel, grid, dim3(kRtThreads), (size_t)n_blocks * sizeof(uint32_t), s, ts,
-                       n_blocks, hkv, causal, k, rho, sigma, top);
+    if (n_blocks <= 256 * kRtPer)
+        hipLaunchKernelGGL(router_topk_kernel<256>, grid, dim3(256), 0, s, ts, n_blocks, hkv, causal, k, rho, sigma,
+                           top);
+    else
+        hipLaunchKernelGGL(router_topk_kernel<1024>, grid, dim3(1024), 0, s, ts, n_blocks, hkv, causal, k, rho, sigma,
+                           top);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int n2 = 1;

@@ -110,6 +110,143 @@ __global__ __launch_bounds__(256) void score_decode_kernel(const T *__restrict__
     out[orow] = best;
 }
 
+// Decode on the matrix cores (bf16 caches): one wave scores 16 chunks for the
+// whole GQA group.  S[chunk][head] = sum_f A[chunk][f] * B[f][head] over 2*D
+// features: envelope A = [kmax | kmin], B = [q+ ; q-] (q+ and q- are exact in
+// bf16, so every product is exact and only the fp32 accumulation rounds);
+// centroid A = [c_hi | c_lo] with the fp32 centroid split into two bf16
+// terms, B = [q ; q].  The group maximum is a 16-lane max over the MFMA
+// columns.  Per chunk this reads the 512-byte metadata row once and issues a
+// handful of instructions, so the kernel stays on the HBM roof for any group
+// size (a vector-ALU form needs 2*g*D FMAs per 512 bytes, at the ridge for
+// g = 8).
+__device__ __forceinline__ uint4 split_sign(uint4 w, bool neg);
+
+template <int D, int KIND>
+__global__ __launch_bounds__(256) void score_decode_mfma_kernel(const uint16_t *__restrict__ q, int hq, KvView kv,
+                                                                ChunkView ch, const uint16_t *__restrict__ kmin,
+                                                                const uint16_t *__restrict__ kmax,
+                                                                const float *__restrict__ cen,
+                                                                float *__restrict__ out) {
+    constexpr int NS = 2 * D / 32;  // MFMA steps over 2*D features
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = hq / kv.hkv;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, G = lane >> 4;
+    const int n = ch.starts ? ch.num[b] : (kv.seq_lens[b] + kv.page - 1) >> kv.log2page;
+    float *orow = out + ((int64_t)b * kv.hkv + h) * ch.max_chunks;
+    bf16x8 bq[NS];
+    {
+        uint4 qv[NS / 2];
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            qv[s] = make_uint4(0, 0, 0, 0);
+            if (n16 < g)
+                qv[s] = *reinterpret_cast<const uint4 *>(q + ((int64_t)b * hq + h * g + n16) * D + 32 * s + 8 * G);
+        }
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            if constexpr (KIND == BSA_ENVELOPE) {
+                bq[s] = __builtin_bit_cast(bf16x8, split_sign(qv[s], false));
+                bq[s + NS / 2] = __builtin_bit_cast(bf16x8, split_sign(qv[s], true));
+            } else {
+                bq[s] = __builtin_bit_cast(bf16x8, qv[s]);
+                bq[s + NS / 2] = bq[s];
+            }
+        }
+    }
+    const int64_t mbase = ((int64_t)b * kv.hkv + h) * ch.max_chunks * D;
+    // chunk groups of 16: wave-strided over the grid, the next group's metadata
+    // in flight while the current one is reduced
+    const int stride = gridDim.x * 4;
+    const int n_groups = (ch.max_chunks + 15) / 16;
+    auto load = [&](int grp, uint4 (&a)[NS]) {
+        const int c = min(grp * 16 + n16, n - 1);  // clamped: always a valid row
+        const int64_t mrow = mbase + (int64_t)c * D;
+        if constexpr (KIND == BSA_ENVELOPE) {
+#pragma unroll
+            for (int s = 0; s < NS / 2; ++s) {
+                a[s] = *reinterpret_cast<const uint4 *>(kmax + mrow + 32 * s + 8 * G);
+                a[s + NS / 2] = *reinterpret_cast<const uint4 *>(kmin + mrow + 32 * s + 8 * G);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS / 2; ++s) {
+                const float4 x0 = *reinterpret_cast<const float4 *>(cen + mrow + 32 * s + 8 * G);
+                const float4 x1 = *reinterpret_cast<const float4 *>(cen + mrow + 32 * s + 8 * G + 4);
+                a[s] = make_uint4(__float_as_uint(x0.x), __float_as_uint(x0.y), __float_as_uint(x0.z),
+                                  __float_as_uint(x0.w));
+                a[s + NS / 2] = make_uint4(__float_as_uint(x1.x), __float_as_uint(x1.y), __float_as_uint(x1.z),
+                                           __float_as_uint(x1.w));
+            }
+        }
+    };
+    auto score = [&](int grp, const uint4 (&araw)[NS]) {
+        const int c0 = grp * 16;
+        uint4 a[NS];
+        if constexpr (KIND == BSA_ENVELOPE) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) a[s] = araw[s];
+        } else {
+            // fp32 centroid -> bf16 hi + lo
+#pragma unroll
+            for (int s = 0; s < NS / 2; ++s) {
+                const uint32_t xw[8] = {araw[s].x, araw[s].y, araw[s].z, araw[s].w,
+                                        araw[s + NS / 2].x, araw[s + NS / 2].y, araw[s + NS / 2].z,
+                                        araw[s + NS / 2].w};
+                uint16_t hi[8], lo[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = __uint_as_float(xw[e]);
+                    hi[e] = f32_to_bf16_rne(x);
+                    lo[e] = f32_to_bf16_rne(x - bf16_to_f32(hi[e]));
+                }
+                a[s] = make_uint4(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16),
+                                  hi[4] | (uint32_t(hi[5]) << 16), hi[6] | (uint32_t(hi[7]) << 16));
+                a[s + NS / 2] = make_uint4(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16),
+                                           lo[4] | (uint32_t(lo[5]) << 16), lo[6] | (uint32_t(lo[7]) << 16));
+            }
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]), bq[s], acc, 0, 0, 0);
+        // lane holds S[chunk 4G+i][head n16]; maximum over the group's heads
+        float m[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = n16 < g ? acc[i] : -INFINITY;
+            v = wave_max_xor(v, 1);
+            v = wave_max_xor(v, 2);
+            v = wave_max_xor(v, 4);
+            v = wave_max_xor(v, 8);
+            m[i] = v;
+        }
+        if (n16 == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int cc = c0 + 4 * G + i;
+                if (cc < ch.max_chunks) orow[cc] = cc < n ? m[i] : -INFINITY;
+            }
+        }
+    };
+    const int first = blockIdx.x * 4 + w;
+    if (first >= n_groups) return;
+    if (n <= 0) {
+        for (int grp = first; grp < n_groups; grp += stride)
+            if (lane < 16 && grp * 16 + lane < ch.max_chunks) orow[grp * 16 + lane] = -INFINITY;
+        return;
+    }
+    uint4 aA[NS], aB[NS];
+    load(first, aA);
+    for (int grp = first; grp < n_groups; grp += 2 * stride) {
+        load(min(grp + stride, n_groups - 1), aB);   // unconditional: exact memory counters
+        score(grp, aA);
+        if (grp + stride >= n_groups) break;
+        load(min(grp + 2 * stride, n_groups - 1), aA);
+        score(grp + stride, aB);
+    }
+}
+
 template <typename T, int D, int KIND>
 static void dispatch_decode_g(const void *q, int hq, const KvView &kv, const ChunkView &ch, const void *kmin,
                               const void *kmax, const float *cen, float *scores, hipStream_t s) {
@@ -139,8 +276,30 @@ static void dispatch_decode_kind(const void *q, int hq, const KvView &kv, const 
 hipError_t launch_score_decode(const void *q, int32_t hq, const KvView &kv, const ChunkView &ch, const void *kmin,
                                const void *kmax, const float *cen, int32_t kind, float *scores, hipStream_t s) {
     if (kv.dtype == BSA_BF16) {
-        if (kv.d == 128) dispatch_decode_kind<uint16_t, 128>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);
-        else dispatch_decode_kind<uint16_t, 64>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);
+        // one 16-chunk group per wave when (sequence, head) pairs are few,
+        // several per wave (q loaded once) when they are many: ~1024 workgroups
+        const int n_groups = (ch.max_chunks + 15) / 16;
+        const int bh = kv.batch * kv.hkv;
+        int gx = (n_groups + 3) / 4;
+        const int want = (1024 + bh - 1) / bh;
+        if (gx > want) gx = want;
+        dim3 grid(gx, kv.hkv, kv.batch), block(256);
+        const uint16_t *qq = (const uint16_t *)q, *mn = (const uint16_t *)kmin, *mx = (const uint16_t *)kmax;
+        if (kv.d == 128) {
+            if (kind == BSA_ENVELOPE)
+                hipLaunchKernelGGL((score_decode_mfma_kernel<128, BSA_ENVELOPE>), grid, block, 0, s, qq, hq, kv, ch, mn,
+                                   mx, cen, scores);
+            else
+                hipLaunchKernelGGL((score_decode_mfma_kernel<128, BSA_CENTROID>), grid, block, 0, s, qq, hq, kv, ch, mn,
+                                   mx, cen, scores);
+        } else {
+            if (kind == BSA_ENVELOPE)
+                hipLaunchKernelGGL((score_decode_mfma_kernel<64, BSA_ENVELOPE>), grid, block, 0, s, qq, hq, kv, ch, mn,
+                                   mx, cen, scores);
+            else
+                hipLaunchKernelGGL((score_decode_mfma_kernel<64, BSA_CENTROID>), grid, block, 0, s, qq, hq, kv, ch, mn,
+                                   mx, cen, scores);
+        }
     } else {
         if (kv.d == 128) dispatch_decode_kind<float, 128>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);
         else dispatch_decode_kind<float, 64>(q, hq, kv, ch, kmin, kmax, cen, kind, scores, s);

@@ -7,48 +7,34 @@
 // int(pages * ratio)) with forced first / last pages).  Variable chunks fill a
 // token budget with the longest prefix of the score order that fits.
 //
-// All three budgets are one weighted radix select.  Candidates are ordered by
-// (score descending, index ascending); with a weight per candidate (1 for
-// chunk counts, the chunk length for token budgets) the selection is the
-// longest prefix of that order whose total weight <= budget.  Four 8-bit
-// passes over order-preserving float keys find the key T of the first
-// candidate that does not fit; every key > T is kept, and the candidates with
-// key == T are kept in ascending index order while their running weight fits.
-// Forced pages get the key 0xffffffff, above every finite score.  The output
-// is written in ascending index order by a block-wide scan, so ties need no
-// sort.  One 256-thread workgroup per row; the keys live in LDS.
+// All three budgets are one weighted radix select (radix_select.h): weight 1
+// per chunk for chunk budgets, the chunk length for token budgets.  Forced
+// pages get the key 0xffffffff, above every finite score, so they are always
+// part of the prefix and count inside K.  One workgroup per row (256 threads
+// up to 2048 chunks, else 1024), 8 consecutive candidates per thread in
+// registers (up to 8192 chunks).
 #include "bsa_internal.h"
 #include "radix_select.h"
 
 namespace bsa {
 
-__device__ __forceinline__ int chunk_weight(const KvView &kv, const ChunkView &ch, int b, int L, int i,
-                                            bool tokens) {
-    if (!tokens) return 1;
-    if (ch.starts) {
-        const int32_t *st = ch.starts + (int64_t)b * (ch.max_chunks + 1);
-        return st[i + 1] - st[i];
-    }
-    const int s = i << kv.log2page;
-    return min(kv.page, L - s);
-}
+constexpr int kSelPer = 8;
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__restrict__ scores, KvView kv,
-                                                             ChunkView ch, bsa_budget bud, int32_t *__restrict__ sel_idx,
-                                                             int32_t *__restrict__ sel_count, int max_sel) {
-    extern __shared__ uint32_t keys[];
-    __shared__ int hist[256];
-    __shared__ int scan[8];
-    __shared__ int bcast[2];
+template <int NT>
+__global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ scores, KvView kv, ChunkView ch,
+                                                        bsa_budget bud, int32_t *__restrict__ sel_idx,
+                                                        int32_t *__restrict__ sel_count, int max_sel) {
+    __shared__ RadixShared sh;
     const int h = blockIdx.x, b = blockIdx.y;
     const int L = kv.seq_lens[b];
     const int n = ch.starts ? ch.num[b] : (L + kv.page - 1) >> kv.log2page;
     const float *row = scores + ((int64_t)b * kv.hkv + h) * ch.max_chunks;
     int64_t budget;
     bool forced_bos = false, forced_eos = false;
+    const bool tokens = bud.mode == BSA_BUDGET_TOKENS;
     if (bud.mode == BSA_BUDGET_TOPK) {
         budget = bud.top_k;
-    } else if (bud.mode == BSA_BUDGET_TOKENS) {
+    } else if (tokens) {
         budget = bud.tokens;
     } else {
         int64_t K = (int64_t)floor((double)n * bud.ratio);
@@ -58,25 +44,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float *__rest
         forced_bos = bud.bos != 0;
         forced_eos = bud.eos != 0;
     }
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-        uint32_t k = float_key(row[i]);
-        if ((forced_bos && i == 0) || (forced_eos && i == n - 1)) k = 0xffffffffu;
-        keys[i] = k;
+    const int base = threadIdx.x * kSelPer;
+    uint32_t keys[kSelPer];
+    int wts[kSelPer];
+    const int32_t *st = ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr;
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) {
+        const int c = base + i;
+        keys[i] = 0u;
+        wts[i] = 1;
+        if (c < n) {
+            uint32_t k = float_key(row[c]);
+            if ((forced_bos && c == 0) || (forced_eos && c == n - 1)) k = 0xffffffffu;
+            keys[i] = k;
+            if (tokens) wts[i] = st ? st[c + 1] - st[c] : min(kv.page, L - (c << kv.log2page));
+        }
     }
-    __syncthreads();
-    const bool tokens = bud.mode == BSA_BUDGET_TOKENS;
     int32_t *dst = sel_idx + ((int64_t)b * kv.hkv + h) * max_sel;
-    auto weight = [&](int i) { return chunk_weight(kv, ch, b, L, i, tokens); };
-    const int cnt = radix_select_prefix(keys, n, budget, weight, dst, max_sel, hist, scan, bcast);
-    for (int i = cnt + threadIdx.x; i < max_sel; i += kSelThreads) dst[i] = -1;
+    const int cnt = radix_select_prefix<NT, kSelPer>(keys, wts, base, n, budget, dst, max_sel, sh);
+    for (int i = cnt + threadIdx.x; i < max_sel; i += NT) dst[i] = -1;
     if (threadIdx.x == 0) sel_count[(int64_t)b * kv.hkv + h] = cnt;
 }
 
 hipError_t launch_select(const float *scores, const KvView &kv, const ChunkView &ch, const bsa_budget &b,
                          int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, hipStream_t s) {
-    dim3 grid(kv.hkv, kv.batch), block(kSelThreads);
-    const size_t lds = (size_t)ch.max_chunks * sizeof(uint32_t);
-    hipLaunchKernelGGL(select_kernel, grid, block, lds, s, scores, kv, ch, b, sel_idx, sel_count, max_sel);
+    dim3 grid(kv.hkv, kv.batch);
+    if (ch.max_chunks <= 256 * kSelPer)
+        hipLaunchKernelGGL(select_kernel<256>, grid, dim3(256), 0, s, scores, kv, ch, b, sel_idx, sel_count, max_sel);
+    else
+        hipLaunchKernelGGL(select_kernel<1024>, grid, dim3(1024), 0, s, scores, kv, ch, b, sel_idx, sel_count,
+                           max_sel);
     return hipGetLastError();
 }
 

@@ -262,7 +262,7 @@ def sparse_attn_decode(q: torch.Tensor, kv: KVCache, sel_idx: Optional[torch.Ten
     items = max_sel if sel_idx is not None else _max_chunks(kv, chunks)
     need = decode_workspace_bytes(kv, Hq, items, num_splits)
     if workspace is None and need:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L = _abi.lib()
     rc = L.bsa_sparse_attn_decode(_ptr(q), Hq, ctypes.byref(kv.struct()), _chunks_struct(chunks), _ptr(sel_idx),

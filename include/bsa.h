@@ -212,7 +212,9 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * bsa_select_topk; sel_idx == NULL attends to every chunk (dense baseline).
  * q [batch][H_q][D] (kv dtype); out [batch][H_q][D] float32.
  * Group size H_q/H_kv <= 16.  workspace >= bsa_decode_workspace_bytes(...)
- * (0 bytes when the resolved split count is 1).
+ * (0 bytes when the resolved split count is 1): the split partials, merged
+ * by a second kernel on the same stream.  Splits are capped at 64.  Calls that
+ * share a workspace must not overlap.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
  */
 int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits);
