@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--extra", action="store_true", help="also the seven-ratio batched sweep")
     ap.add_argument("--only-headline-kernel", action="store_true",
                     help="profiling aid: time only the headline workload")
+    ap.add_argument("--kernel-launches", type=int, default=200, help="launches per per-kernel timing loop")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="profiling aid: after timing, copy this many MiB device-to-device once (a plain copy of "
+                         "known size to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -193,13 +197,13 @@ class DecodeBench:
         qo = B * Hq * D * (2 + 4)
         return meta, kvb, qo, dense_kv
 
-    def measure(self, steps, warmup):
+    def measure(self, steps, warmup, launches=200):
         t_step = self.time_steps(steps, warmup)
         self.step(0)
-        t_attn = self.time_kernel(self.attend)
-        t_dense = self.time_kernel(self.dense)
-        t_sel = self.time_kernel(self.select)
-        t_meta = self.time_kernel(self.meta)
+        t_attn = self.time_kernel(self.attend, launches)
+        t_dense = self.time_kernel(self.dense, launches)
+        t_sel = self.time_kernel(self.select, launches)
+        t_meta = self.time_kernel(self.meta, launches)
         meta_b, kv_b, qo_b, dense_b = self.bytes()
         return {"t_step": t_step, "t_attn": t_attn, "t_dense": t_dense, "t_select": t_sel, "t_meta": t_meta,
                 "meta_bytes": meta_b, "kv_bytes": kv_b, "qo_bytes": qo_b, "dense_kv_bytes": dense_b}
@@ -321,6 +325,28 @@ class PrefillBench:
         }
 
 
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_paged16_replay_b1_hbm_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline decode call from the committed
+    FETCH_SIZE / WRITE_SIZE summary, or None when that summary was taken on a
+    different version of the decode kernel source."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(PMC_SUMMARY):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        src = os.path.join(ROOT, "block_sparse_attention_chunk_amd", "csrc", "decode.hip")
+        if hashlib.sha1(open(src, "rb").read()).hexdigest() != fields.get("decode_source_sha1"):
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(case, k_pages, scoring, seconds):
     """The fp64 oracle on the host cores on the same inputs and stages (score +
     select + attention per step, metadata built once), run for ~`seconds`."""
@@ -358,7 +384,7 @@ def main():
     case = synth.replay_decode()
     k_pages = a.budget // case.page_size
     hb = DecodeBench(case, ops.Budget.topk(k_pages), a.scoring, dev, a.replicas_gib)
-    m = hb.measure(a.steps, a.warmup)
+    m = hb.measure(a.steps, a.warmup, a.kernel_launches)
     head = record(f"replay-shaped decode, {case.num_q_heads} q / {case.num_kv_heads} KV heads, d 128, bf16, "
                   f"{int(case.seq_lens[0])} tokens, {a.scoring} scoring, top-{k_pages} of "
                   f"{int(case.n_chunks()[0])} 16-token pages (budget {k_pages * 16} tokens), 1 sequence", hb, m)
@@ -381,9 +407,10 @@ def main():
                    "splits": hb.splits, "cache_replicas": hb.replicas, "graph_replay": True},
         "effective_hbm_gbs": head["effective_hbm_gbs"],
         "effective_hbm_frac": head["effective_hbm_frac"],
-        "roofline": {"bound": "hbm", "kernel": "decode_paged16_kernel (bsa_sparse_attn_decode, merge fused)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "bsa_sparse_attn_decode (decode_paged16_kernel + decode_merge_kernel)",
                      "achieved": head["selected_kv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["selected_kv_frac"], "traffic": None},
+                     "frac": head["selected_kv_frac"], "traffic": measured_traffic()},
         "headline": head,
     }
     del hb
@@ -428,6 +455,14 @@ def main():
                 del b3
                 torch.cuda.empty_cache()
         res["ratio_sweep"] = sweep
+    if a.calibration_copy_mib:
+        n = a.calibration_copy_mib * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(case, k_pages, a.scoring, a.cpu_seconds)
