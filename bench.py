@@ -5,9 +5,15 @@ Headline workload: one decode layer shaped like the replay study's model
 (32 q / 4 KV heads, head_dim 128, bf16, 16-token pages) at 29,504 cached tokens
 with a 4096-token budget (top 256 of 1,844 pages), envelope scoring, one
 sequence.  One step = chunk scoring + per-KV-head top-k + split-K sparse
-attention (merge included) for the whole batch.  Chunk metadata is built once
+attention + split merge for the whole batch, run as the library's decode step:
+bsa_score_chunks then bsa_select_attn_decode (selection fused into the
+attention kernel).  The unfused sequence (bsa_select_topk then
+bsa_sparse_attn_decode) is timed beside it.  Chunk metadata is built once
 before timing (in a live loop a page's metadata is written once per 16 decode
-steps) and its build time is reported apart.
+steps) and its build time is reported apart.  Per-kernel figures (the fused
+kernel, the decode kernel and the merge alone) come from HIP events around
+graph replays of that launch alone on its stream (the split partials are left
+in the workspace and merged by a separate call).
 
 Inputs are synthetic and seeded (block_sparse_attention_chunk_amd/synth.py)
 and resident in HBM before the timed region.  Steps rotate over replicas of
@@ -105,6 +111,10 @@ class DecodeBench:
         self.dense_splits = ops.decode_num_splits(kv0, case.num_q_heads, kv0.max_pages)
 
     # --- the hot path ---------------------------------------------------------------
+    def score(self, r):
+        kv, meta = self.reps[r]
+        self.ops.score_chunks(self.q, kv, meta, self.kind, out=self.scores)
+
     def select(self, r):
         ops = self.ops
         kv, meta = self.reps[r]
@@ -115,7 +125,32 @@ class DecodeBench:
         kv, _ = self.reps[r]
         self.ops.sparse_attn_decode(self.q, kv, self.sel, self.cnt, out=self.out, workspace=self.ws)
 
+    def decode_kernel(self, r):
+        kv, _ = self.reps[r]
+        self.ops.sparse_attn_decode(self.q, kv, self.sel, self.cnt, out=self.partials_or_out(), workspace=self.ws)
+
+    def merge(self, r):
+        self.ops.decode_merge(self.ws, self.case.batch, self.case.num_q_heads, self.case.head_dim, self.splits,
+                              out=self.out)
+
+    def fused(self, r):
+        kv, _ = self.reps[r]
+        self.ops.select_attn_decode(self.q, kv, self.scores, self.budget, out=self.out, workspace=self.ws)
+
+    def fused_kernel(self, r):
+        kv, _ = self.reps[r]
+        self.ops.select_attn_decode(self.q, kv, self.scores, self.budget, out=self.partials_or_out(),
+                                    workspace=self.ws)
+
+    def partials_or_out(self):
+        return self.ops.PARTIALS if self.splits > 1 else self.out
+
     def step(self, r):
+        """The decode step: scores, then selection + attention + merge."""
+        self.score(r)
+        self.fused(r)
+
+    def step_unfused(self, r):
         self.select(r)
         self.attend(r)
 
@@ -140,34 +175,41 @@ class DecodeBench:
         torch.cuda.synchronize()
         return g
 
-    def time_steps(self, steps, warmup):
-        """Exactly `steps` decode steps, rotating replicas, from HIP graphs."""
+    def time_steps(self, steps, warmup, fn=None):
+        """Exactly `steps` decode steps, rotating replicas, from HIP graphs.  A
+        graph holds whole rounds over the replicas, at least 16 steps, so the
+        replay's host overhead stays hidden behind the device work."""
         torch = self.torch
+        fn = fn or self.step
         R = self.replicas
-        g_all = self.graph(self.step, range(R))
-        g_one = [self.graph(self.step, [r]) for r in range(R)]
+        rounds = max(1, math.ceil(16 / R))
+        g_block = self.graph(fn, list(range(R)) * rounds)
+        g_one = [self.graph(fn, [r]) for r in range(R)]
+        per_block = R * rounds
 
-        def run(n, start):
-            full, rem = divmod(n, R)
+        def run(n):
+            full, rem = divmod(n, per_block)
             for _ in range(full):
-                g_all.replay()
+                g_block.replay()
             for r in range(rem):
-                g_one[(start + r) % R].replay()
+                g_one[r % R].replay()
 
-        run(warmup, 0)
+        run(warmup)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run(steps, 0)
+        run(steps)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
     def time_kernel(self, fn, min_launches=200):
-        """Average duration of one launch of fn: back-to-back launches over all
-        replicas in one graph, bracketed by HIP events on the launch stream."""
+        """Average duration of one launch of fn: back-to-back launches over the
+        replicas (at least 32 per graph), bracketed by HIP events on the launch
+        stream."""
         torch = self.torch
         R = self.replicas
-        per = max(1, math.ceil(min_launches / R))
-        g = self.graph(fn, list(range(R)) * 1)
+        reps = list(range(R)) * max(1, math.ceil(32 / R))
+        per = max(1, math.ceil(min_launches / len(reps)))
+        g = self.graph(fn, reps)
         stream = torch.cuda.current_stream(self.dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g.replay()
@@ -176,7 +218,7 @@ class DecodeBench:
             g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / (per * R)
+        return e0.elapsed_time(e1) * 1e-3 / (per * len(reps))
 
     def bytes(self):
         """Algorithmic bytes of one step: metadata read + selected K/V + q in + out."""
@@ -199,30 +241,47 @@ class DecodeBench:
 
     def measure(self, steps, warmup, launches=200):
         t_step = self.time_steps(steps, warmup)
-        self.step(0)
-        t_attn = self.time_kernel(self.attend, launches)
-        t_dense = self.time_kernel(self.dense, launches)
-        t_sel = self.time_kernel(self.select, launches)
-        t_meta = self.time_kernel(self.meta, launches)
+        t_step_unfused = self.time_steps(steps, warmup, self.step_unfused)
+        self.step_unfused(0)
+        self.torch.cuda.synchronize()
+        m = {"t_step": t_step, "t_step_unfused": t_step_unfused,
+             "t_fused": self.time_kernel(self.fused, launches),
+             "t_fused_kernel": self.time_kernel(self.fused_kernel, launches),
+             "t_attn": self.time_kernel(self.attend, launches),
+             "t_decode_kernel": self.time_kernel(self.decode_kernel, launches),
+             "t_dense": self.time_kernel(self.dense, launches),
+             "t_score": self.time_kernel(self.score, launches),
+             "t_select": self.time_kernel(self.select, launches),
+             "t_meta": self.time_kernel(self.meta, launches)}
+        self.decode_kernel(0)
+        m["t_merge"] = self.time_kernel(self.merge, launches) if self.splits > 1 else 0.0
         meta_b, kv_b, qo_b, dense_b = self.bytes()
-        return {"t_step": t_step, "t_attn": t_attn, "t_dense": t_dense, "t_select": t_sel, "t_meta": t_meta,
-                "meta_bytes": meta_b, "kv_bytes": kv_b, "qo_bytes": qo_b, "dense_kv_bytes": dense_b}
+        m.update({"meta_bytes": meta_b, "kv_bytes": kv_b, "qo_bytes": qo_b, "dense_kv_bytes": dense_b})
+        return m
 
 
 def record(name, bench, m):
     case = bench.case
     step_bytes = m["meta_bytes"] + m["kv_bytes"] + m["qo_bytes"]
+    kvb = m["kv_bytes"]
     return {
         "workload": name,
         "batch": case.batch, "seq_len": int(case.seq_lens.max()), "q_heads": case.num_q_heads,
         "kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "scoring": bench.scoring,
         "tokens_per_s": case.batch / m["t_step"],
         "us_per_step": m["t_step"] * 1e6,
+        "unfused_us_per_step": m["t_step_unfused"] * 1e6,
         "effective_hbm_gbs": step_bytes / m["t_step"] / 1e9,
         "effective_hbm_frac": step_bytes / m["t_step"] / 1e9 / HBM_PEAK_GBS,
+        "score_us": m["t_score"] * 1e6,
+        "fused_select_attn_us": m["t_fused"] * 1e6,
+        "fused_kernel_us": m["t_fused_kernel"] * 1e6,
+        "fused_kernel_selected_kv_gbs": kvb / m["t_fused_kernel"] / 1e9,
         "sparse_attn_us": m["t_attn"] * 1e6,
-        "selected_kv_gbs": m["kv_bytes"] / m["t_attn"] / 1e9,
-        "selected_kv_frac": m["kv_bytes"] / m["t_attn"] / 1e9 / HBM_PEAK_GBS,
+        "decode_kernel_us": m["t_decode_kernel"] * 1e6,
+        "merge_kernel_us": m["t_merge"] * 1e6,
+        "selected_kv_gbs": kvb / m["t_decode_kernel"] / 1e9,
+        "selected_kv_frac": kvb / m["t_decode_kernel"] / 1e9 / HBM_PEAK_GBS,
         "score_select_us": m["t_select"] * 1e6,
         "meta_build_us": m["t_meta"] * 1e6,
         "dense_attn_us": m["t_dense"] * 1e6,
@@ -231,7 +290,7 @@ def record(name, bench, m):
         "speedup_step_vs_dense": m["t_dense"] / m["t_step"],
         "splits": bench.splits,
         "cache_replicas": bench.replicas,
-        "bytes_per_step": {"metadata": m["meta_bytes"], "selected_kv": m["kv_bytes"], "q_out": m["qo_bytes"]},
+        "bytes_per_step": {"metadata": m["meta_bytes"], "selected_kv": kvb, "q_out": m["qo_bytes"]},
     }
 
 
@@ -325,22 +384,30 @@ class PrefillBench:
         }
 
 
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_paged16_replay_b1_hbm_traffic.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_decode_replay_b1_hbm_traffic.txt")
+KERNEL_SOURCES = ["select_decode.hip", "decode_common.h", "radix_select.h", "select_rules.h"]
+
+
+def kernel_source_hash():
+    """sha1 over the sources of the headline fused kernel."""
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_chunk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
-    """HBM bytes per launch of the headline decode call from the committed
+    """HBM bytes per launch of the headline fused kernel from the committed
     FETCH_SIZE / WRITE_SIZE summary, or None when that summary was taken on a
-    different version of the decode kernel source."""
-    import hashlib
+    different version of the kernel's sources."""
     try:
         fields = {}
         for line in open(PMC_SUMMARY):
             if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-        src = os.path.join(ROOT, "block_sparse_attention_chunk_amd", "csrc", "decode.hip")
-        if hashlib.sha1(open(src, "rb").read()).hexdigest() != fields.get("decode_source_sha1"):
+        if kernel_source_hash() != fields.get("kernel_source_sha1"):
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -408,9 +475,11 @@ def main():
         "effective_hbm_gbs": head["effective_hbm_gbs"],
         "effective_hbm_frac": head["effective_hbm_frac"],
         "roofline": {"bound": "hbm",
-                     "kernel": "bsa_sparse_attn_decode (decode_paged16_kernel + decode_merge_kernel)",
-                     "achieved": head["selected_kv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["selected_kv_frac"], "traffic": measured_traffic()},
+                     "kernel": "select_decode_kernel (bsa_select_attn_decode without the merge)",
+                     "achieved": head["fused_kernel_selected_kv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["fused_kernel_selected_kv_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": m["kv_bytes"],
+                     "launch_us": m["t_fused_kernel"] * 1e6},
         "headline": head,
     }
     del hb

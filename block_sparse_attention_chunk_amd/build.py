@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 
-SOURCES = ["api.cpp", "meta.hip", "score.hip", "select.hip", "router.hip", "decode.hip", "tile_prefill.hip"]
+SOURCES = ["api.cpp", "meta.hip", "score.hip", "select.hip", "router.hip", "decode.hip", "select_decode.hip", "tile_prefill.hip"]
 ARCH = "gfx950"
 # Packed fp32 vector ops stay off: the compiler keeps plain v_fma_f32 / v_mul_f32.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

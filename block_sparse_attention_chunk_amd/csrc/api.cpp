@@ -94,9 +94,38 @@ int launched(hipError_t e) {
     return ok();
 }
 
+// The largest number of chunks a row of max_chunks can keep under *budget.
+int budget_need(const bsa_budget *budget, int max_chunks, int64_t *need) {
+    switch (budget->mode) {
+    case BSA_BUDGET_TOPK:
+        if (budget->top_k < 1) return fail(BSA_ERR_INVALID_ARG, "top_k must be >= 1");
+        *need = budget->top_k < max_chunks ? budget->top_k : max_chunks;
+        return BSA_OK;
+    case BSA_BUDGET_TOKENS:
+        if (budget->tokens < 1) return fail(BSA_ERR_INVALID_ARG, "tokens must be >= 1");
+        *need = budget->tokens < max_chunks ? budget->tokens : max_chunks;
+        return BSA_OK;
+    case BSA_BUDGET_RATIO: {
+        if (!(budget->ratio > 0.0 && budget->ratio <= 1.0))
+            return fail(BSA_ERR_INVALID_ARG, "ratio must be in (0, 1]");
+        if ((budget->bos != 0 && budget->bos != 1) || (budget->eos != 0 && budget->eos != 1))
+            return fail(BSA_ERR_INVALID_ARG, "bos and eos must be 0 or 1");
+        int64_t K = (int64_t)std::floor((double)max_chunks * budget->ratio);
+        const int64_t forced = 1 + budget->bos + budget->eos;
+        if (K < forced) K = forced;
+        *need = K < max_chunks ? K : max_chunks;
+        return BSA_OK;
+    }
+    default:
+        return fail(BSA_ERR_INVALID_ARG, "budget mode %d is not a BSA_BUDGET_* value", budget->mode);
+    }
+}
+
 constexpr int kMaxSelectChunks = 8192;
 constexpr int kMaxRouterBlocks = 8192;
 constexpr int kMaxRouterTiles = 8192;
+
+constexpr int kMaxItemsPerSplit = 2048;  // the fused selection keeps one split's pages in LDS
 
 int resolve_splits(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
     if (num_splits > 0) return num_splits;
@@ -104,6 +133,8 @@ int resolve_splits(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
     int s = (512 + bh - 1) / bh;                        // aim at ~512 workgroups (2 per CU, 3 resident)
     const int cap = (max_items + 7) / 8;                // at least ~8 items per workgroup
     if (s > cap) s = cap;
+    const int floor_s = (max_items + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit;
+    if (s < floor_s) s = floor_s;
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     return s;
@@ -193,29 +224,7 @@ int bsa_select_topk(const float *scores, const bsa_kv *kv, const bsa_chunks *chu
         return fail(BSA_ERR_UNSUPPORTED, "max_chunks %d exceeds %d", c.max_chunks, kMaxSelectChunks);
     if (max_sel < 1) return fail(BSA_ERR_INVALID_ARG, "max_sel must be >= 1");
     int64_t need;
-    switch (budget->mode) {
-    case BSA_BUDGET_TOPK:
-        if (budget->top_k < 1) return fail(BSA_ERR_INVALID_ARG, "top_k must be >= 1");
-        need = budget->top_k < c.max_chunks ? budget->top_k : c.max_chunks;
-        break;
-    case BSA_BUDGET_TOKENS:
-        if (budget->tokens < 1) return fail(BSA_ERR_INVALID_ARG, "tokens must be >= 1");
-        need = budget->tokens < c.max_chunks ? budget->tokens : c.max_chunks;
-        break;
-    case BSA_BUDGET_RATIO: {
-        if (!(budget->ratio > 0.0 && budget->ratio <= 1.0))
-            return fail(BSA_ERR_INVALID_ARG, "ratio must be in (0, 1]");
-        if ((budget->bos != 0 && budget->bos != 1) || (budget->eos != 0 && budget->eos != 1))
-            return fail(BSA_ERR_INVALID_ARG, "bos and eos must be 0 or 1");
-        int64_t K = (int64_t)std::floor((double)c.max_chunks * budget->ratio);
-        const int64_t forced = 1 + budget->bos + budget->eos;
-        if (K < forced) K = forced;
-        need = K < c.max_chunks ? K : c.max_chunks;
-        break;
-    }
-    default:
-        return fail(BSA_ERR_INVALID_ARG, "budget mode %d is not a BSA_BUDGET_* value", budget->mode);
-    }
+    if ((rc = budget_need(budget, c.max_chunks, &need))) return rc;
     if (max_sel < need)
         return fail(BSA_ERR_INVALID_ARG, "max_sel %d is smaller than the largest possible selection %lld", max_sel,
                     (long long)need);
@@ -273,7 +282,7 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
     if (rc) return rc;
     if ((rc = check_chunks(kv, chunks, &c))) return rc;
     if ((rc = check_heads(kv, num_q_heads, 16))) return rc;
-    if (!q || !out) return fail(BSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if (!q) return fail(BSA_ERR_INVALID_ARG, "q must be non-NULL");
     if (!aligned16(q)) return fail(BSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
     if (sel_idx && (!sel_count || max_sel < 1))
         return fail(BSA_ERR_INVALID_ARG, "sel_idx needs sel_count and max_sel >= 1");
@@ -282,11 +291,64 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
     if (num_splits < 0) return fail(BSA_ERR_INVALID_ARG, "num_splits must be >= 0");
     const int items = sel_idx ? max_sel : c.max_chunks;
     const int splits = resolve_splits(kv, items, num_splits);
+    if (!out && splits == 1)
+        return fail(BSA_ERR_INVALID_ARG, "out may be NULL only with more than one split (partials stay in the "
+                                         "workspace)");
     const size_t need = bsa_decode_workspace_bytes(kv, num_q_heads, items, splits);
     if (need && (!workspace || workspace_bytes < need))
         return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);
     return launched(bsa::launch_decode(q, num_q_heads, v, c, sel_idx, sel_count, max_sel, softmax_scale, splits, out,
                                        workspace, (hipStream_t)stream));
+}
+
+int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
+                           const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
+                           int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    bsa::KvView v;
+    int rc = check_kv(kv, true, &v);
+    if (rc) return rc;
+    if ((rc = check_heads(kv, num_q_heads, 16))) return rc;
+    if (!q || !scores || !budget) return fail(BSA_ERR_INVALID_ARG, "q, scores and budget must be non-NULL");
+    if (!aligned16(q)) return fail(BSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if (kv->page_size != 16) return fail(BSA_ERR_UNSUPPORTED, "fused selection needs 16-token pages");
+    if (kv->max_pages > kMaxSelectChunks)
+        return fail(BSA_ERR_UNSUPPORTED, "max_pages %d exceeds %d", kv->max_pages, kMaxSelectChunks);
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+        return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+    if (num_splits < 0 || num_splits > 64) return fail(BSA_ERR_INVALID_ARG, "num_splits must be in [0, 64]");
+    int64_t need;
+    if ((rc = budget_need(budget, kv->max_pages, &need))) return rc;
+    if ((sel_idx == nullptr) != (sel_count == nullptr))
+        return fail(BSA_ERR_INVALID_ARG, "sel_idx and sel_count are both given or both NULL");
+    if (sel_idx && max_sel < need)
+        return fail(BSA_ERR_INVALID_ARG, "max_sel %d is smaller than the largest possible selection %lld", max_sel,
+                    (long long)need);
+    const int splits = resolve_splits(kv, (int)need, num_splits);
+    if ((need + splits - 1) / splits > kMaxItemsPerSplit)
+        return fail(BSA_ERR_INVALID_ARG, "%d splits keep more than %d pages each; use more splits", splits,
+                    kMaxItemsPerSplit);
+    if (!out && splits == 1)
+        return fail(BSA_ERR_INVALID_ARG, "out may be NULL only with more than one split (partials stay in the "
+                                         "workspace)");
+    const size_t ws_need = bsa_decode_workspace_bytes(kv, num_q_heads, (int)need, splits);
+    if (ws_need && (!workspace || workspace_bytes < ws_need))
+        return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", ws_need, workspace_bytes);
+    return launched(bsa::launch_select_decode(q, num_q_heads, v, scores, *budget, sel_idx, sel_count,
+                                              sel_idx ? max_sel : 0, softmax_scale, splits, out, workspace,
+                                              (hipStream_t)stream));
+}
+
+int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                     int32_t num_splits, float *out, void *stream) {
+    if (!workspace || !out) return fail(BSA_ERR_INVALID_ARG, "workspace and out must be non-NULL");
+    if (batch < 1 || num_q_heads < 1) return fail(BSA_ERR_INVALID_ARG, "batch and num_q_heads must be >= 1");
+    if (head_dim != 64 && head_dim != 128) return fail(BSA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", head_dim);
+    if (num_splits < 2 || num_splits > 64) return fail(BSA_ERR_INVALID_ARG, "num_splits must be in [2, 64]");
+    const float *part_o = (const float *)workspace;
+    const float *part_ml = part_o + (size_t)batch * num_q_heads * num_splits * head_dim;
+    return launched(bsa::launch_decode_merge(num_splits, part_o, part_ml, out, num_q_heads, batch, head_dim,
+                                             (hipStream_t)stream));
 }
 
 int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num_rows, const bsa_kv *kv,

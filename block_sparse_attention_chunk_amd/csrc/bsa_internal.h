@@ -103,6 +103,11 @@ hipError_t launch_router(const float *ts, int32_t n_tiles, int32_t hkv, int32_t 
 hipError_t launch_decode(const void *q, int32_t hq, const KvView &kv, const ChunkView &ch, const int32_t *sel_idx,
                          const int32_t *sel_count, int32_t max_sel, float scale, int32_t splits, float *out,
                          void *ws, hipStream_t s);
+hipError_t launch_decode_merge(int splits, const float *part_o, const float *part_ml, float *out, int hq, int batch,
+                               int d, hipStream_t s);
+hipError_t launch_select_decode(const void *q, int32_t hq, const KvView &kv, const float *scores,
+                                const bsa_budget &bud, int32_t *sel_idx, int32_t *sel_count, int32_t max_sel,
+                                float scale, int32_t splits, float *out, void *ws, hipStream_t s);
 hipError_t launch_tile_prefill(const void *q, int32_t hq, int32_t rows, const KvView &kv, int32_t tile_rows,
                                const int32_t *kv_idx, int32_t idx_stride, float scale, float *out, hipStream_t s);
 

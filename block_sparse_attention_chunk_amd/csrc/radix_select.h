@@ -1,5 +1,5 @@
 // radix_select.h -- weighted radix select of a score-order prefix, shared by
-// the decode selection and the router.
+// the decode selection, the fused selection + decode kernel and the router.
 //
 // Candidates are ordered by (score descending, index ascending).  With a
 // weight per candidate, the selection is the longest prefix of that order
@@ -7,10 +7,17 @@
 // order-preserving float keys find the key T of the first candidate that does
 // not fit; every key > T is kept, and the candidates with key == T are kept in
 // ascending index order while their running weight still fits.  The kept ids
-// come out in ascending index order from a block scan, so ties need no sort.
+// come out in ascending index order from one block scan, so ties need no sort.
 //
 // One workgroup of NT threads per row; each thread holds PER consecutive
-// candidates in registers (n <= NT * PER).
+// candidates in registers (n <= NT * PER).  Per pass: histogram atomics into
+// one of three rotating LDS histograms (two sub-histograms, even / odd waves),
+// one barrier, then every wave finds the crossing digit itself (lane l owns
+// digits 255-4l .. 252-4l, a DPP wave scan gives the weight above them), so
+// no second barrier broadcasts it.  A
+// histogram is cleared two passes after it was read, so clearing needs no
+// barrier of its own.  The total weight falls out of the first pass, and the
+// passes stop early when the cut lands on a digit boundary.
 #pragma once
 
 #include "bsa_internal.h"
@@ -18,140 +25,187 @@
 namespace bsa {
 
 struct RadixShared {
-    int hist[256];
-    int wsum[32];       // per-wave partial sums of the block scans
-    int digit, wabove;
-    long long total;
+    int hist[3][2][256];
+    int wsum[2][16];    // per-wave partials of the block scan (<= 16 waves)
+    int esel;           // number of kept candidates with key == T (-1: all of them)
 };
 
-// Inclusive block scan of v over NT threads; *total receives the block sum.
-template <int NT>
-__device__ __forceinline__ int block_scan_incl(int v, RadixShared &sh, int *total) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) sh.wsum[wid] = x;
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int s = sh.wsum[w];
-        off += (w < wid) ? s : 0;
-        tot += s;
-    }
-    __syncthreads();
-    *total = tot;
-    return x + off;
+// Inclusive scan over the 64 lanes of a wave with DPP: shifts 1, 2, 4, 8 inside
+// each row of 16 (lanes before the row start add 0), then the last lane of
+// each row into the next row (rows 1, 3) and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
 }
 
-// keys[PER] / wts[PER]: this thread's candidates (index base + i, valid when
-// base + i < n).  Returns the number kept; writes the kept indices ascending to
-// dst[0 .. min(count, dst_cap)).
+// Inclusive block scan of two values at once over NT threads; totals in ta /
+// tb.  Single use per kernel phase: the per-wave partials are not protected
+// against a second scan that starts before every wave has read them.
+template <int NT>
+__device__ __forceinline__ void block_scan_pair(int &a, int &b, RadixShared &sh, int &ta, int &tb) {
+    constexpr int NW = NT / 64;
+    static_assert(NW <= 16, "at most 16 waves");
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    a = wave_scan_incl(a);
+    b = wave_scan_incl(b);
+    if (lane == 63) {
+        sh.wsum[0][wid] = a;
+        sh.wsum[1][wid] = b;
+    }
+    __syncthreads();
+    int oa = 0, ob = 0;
+    ta = 0, tb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int x = sh.wsum[0][w], y = sh.wsum[1][w];
+        oa += (w < wid) ? x : 0;
+        ob += (w < wid) ? y : 0;
+        ta += x;
+        tb += y;
+    }
+    a += oa;
+    b += ob;
+}
+
+// keys[PER] / wts[PER] (weights >= 1): this thread's candidates (index
+// base + i, valid when base + i < n <= 65535).  Returns the number kept;
+// emit(pos, index, i) is called once for every kept candidate, pos being its
+// rank in ascending index order and i its slot in this thread's arrays.  The total weight must stay below 2^31.
+template <int NT, int PER, typename Emit>
+__device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[PER], const int (&wts)[PER], int base,
+                                                        int n, int64_t budget, Emit emit, RadixShared &sh) {
+    const int tid = threadIdx.x, lane = tid & 63, sub = (tid >> 6) & 1;
+    const int bud = (int)min(budget, (int64_t)0x7fffffff);
+    int *flat0 = &sh.hist[0][0][0];
+    for (int i = tid; i < 512; i += NT) flat0[i] = 0;
+    if (tid == 0) sh.esel = -1;
+    __syncthreads();
+
+    bool all = false;
+    uint32_t prefix = 0, pmask = 0;
+    int wabove = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        int(*H)[256] = sh.hist[pass % 3];
+        int *next = &sh.hist[(pass + 1) % 3][0][0];  // last read two passes ago
+        for (int i = tid; i < 512; i += NT) next[i] = 0;
+        // consecutive candidates mostly share a digit (scores of neighbouring
+        // chunks have similar magnitude): a run of equal digits is added once,
+        // by its last element (straight-line code, one predicated atomic per
+        // element)
+        bool m[PER];
+        int dg[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            m[i] = base + i < n && (keys[i] & pmask) == prefix;
+            dg[i] = (keys[i] >> shift) & 255u;
+        }
+        int acc = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            acc += m[i] ? wts[i] : 0;
+            bool last = m[i];
+            if (i + 1 < PER) last = last && !(m[i + 1] && dg[i + 1] == dg[i]);
+            if (last) atomicAdd(&H[sub][dg[i]], acc);
+            acc = last ? 0 : acc;
+        }
+        __syncthreads();
+        // every wave: lane l holds digits 255-4l .. 252-4l (descending)
+        int h[4], s = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = H[0][255 - 4 * lane - j] + H[1][255 - 4 * lane - j];
+            s += h[j];
+        }
+        const int x = wave_scan_incl(s);
+        if (pass == 0 && __builtin_amdgcn_readlane(x, 63) <= bud) {  // everything fits
+            all = true;
+            break;
+        }
+        int before = wabove + x - s;  // weight of all higher digits
+        int dsel = -1, bsel = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (before <= bud && before + h[j] > bud) {
+                dsel = 255 - 4 * lane - j;
+                bsel = before;
+            }
+            before += h[j];
+        }
+        // exactly one lane holds the crossing digit (the bucket's weight exceeds
+        // what is left of the budget)
+        const int src = max(__builtin_ffsll((long long)__ballot(dsel >= 0)) - 1, 0);
+        const int digit = __builtin_amdgcn_readlane(dsel, src);
+        wabove = __builtin_amdgcn_readlane(bsel, src);
+        prefix |= uint32_t(digit) << shift;
+        pmask |= 255u << shift;
+        if (wabove == bud) {  // the cut is a digit boundary: nothing with this prefix is kept
+            prefix |= ~pmask;
+            pmask = 0xffffffffu;
+            break;
+        }
+    }
+    const uint32_t T = prefix;
+    const int remaining = bud - wabove;
+
+    // one scan of (count > T | count == T << 16, weight == T): ranks of the
+    // kept candidates in index order
+    int gtc = 0, eqc = 0, eqw = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (base + i < n) {
+            const bool gt = all || keys[i] > T, eq = !all && keys[i] == T;
+            gtc += gt ? 1 : 0;
+            eqc += eq ? 1 : 0;
+            eqw += eq ? wts[i] : 0;
+        }
+    }
+    int a = gtc | (eqc << 16), b = eqw, ta, tb;
+    block_scan_pair<NT>(a, b, sh, ta, tb);
+    a -= gtc | (eqc << 16);
+    b -= eqw;
+    int gt_before = a & 0xffff, eq_before = a >> 16;
+    // the first candidate == T that no longer fits: its tie rank is the number
+    // of ties kept (none such: every tie is kept)
+    if (!all) {
+        int ce = eq_before, r = b;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (base + i < n && keys[i] == T) {
+                if (r <= remaining && r + wts[i] > remaining) sh.esel = ce;
+                r += wts[i];
+                ++ce;
+            }
+        }
+    }
+    __syncthreads();
+    const int e_sel = sh.esel < 0 ? (ta >> 16) : sh.esel;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (base + i < n) {
+            const bool gt = all || keys[i] > T, eq = !all && keys[i] == T;
+            if (gt || (eq && eq_before < e_sel)) emit(gt_before + min(eq_before, e_sel), base + i, i);
+            gt_before += gt ? 1 : 0;
+            eq_before += eq ? 1 : 0;
+        }
+    }
+    (void)tb;
+    return (ta & 0xffff) + e_sel;
+}
+
+// As above, writing the kept indices ascending to dst[0 .. min(count, dst_cap));
+// returns min(count, dst_cap).
 template <int NT, int PER>
 __device__ __forceinline__ int radix_select_prefix(const uint32_t (&keys)[PER], const int (&wts)[PER], int base,
                                                    int n, int64_t budget, int *dst, int dst_cap, RadixShared &sh) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    int my_w = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) my_w += (base + i < n) ? wts[i] : 0;
-    int tot;
-    (void)block_scan_incl<NT>(my_w, sh, &tot);
-    const bool all = (int64_t)tot <= budget;
-    uint32_t T = 0;
-    int remaining = 0;
-    if (!all) {
-        uint32_t prefix = 0, pmask = 0;
-        int wabove = 0;
-        const int bud = (int)budget;  // < tot
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-            __syncthreads();
-            // consecutive candidates mostly share a digit (scores of neighbouring
-            // chunks have similar magnitude): add runs of equal digits at once
-            int run_d = -1, run_w = 0;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                if (base + i < n && (keys[i] & pmask) == prefix) {
-                    const int d = (keys[i] >> shift) & 255u;
-                    if (d != run_d) {
-                        if (run_w) atomicAdd(&sh.hist[run_d], run_w);
-                        run_d = d;
-                        run_w = 0;
-                    }
-                    run_w += wts[i];
-                }
-            }
-            if (run_w) atomicAdd(&sh.hist[run_d], run_w);
-            __syncthreads();
-            if (tid < 64) {
-                // lane L holds digits 255-4L .. 252-4L (descending)
-                int h[4], s = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h[j] = sh.hist[255 - 4 * lane - j];
-                    s += h[j];
-                }
-                int x = s;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int y = __shfl_up(x, o, 64);
-                    if (lane >= o) x += y;
-                }
-                int before = wabove + x - s;  // weight of all higher digits
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (before <= bud && before + h[j] > bud) {
-                        sh.digit = 255 - 4 * lane - j;
-                        sh.wabove = before;
-                    }
-                    before += h[j];
-                }
-            }
-            __syncthreads();
-            prefix |= uint32_t(sh.digit) << shift;
-            pmask |= 255u << shift;
-            wabove = sh.wabove;
-        }
-        T = prefix;
-        remaining = bud - wabove;
-    }
-    // weight of this thread's key == T candidates, then their running prefix
-    int eqw = 0;
-    if (!all) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) eqw += (base + i < n && keys[i] == T) ? wts[i] : 0;
-    }
-    int teq;
-    int run = block_scan_incl<NT>(eqw, sh, &teq) - eqw;  // exclusive
-    bool sel[PER];
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const bool valid = base + i < n;
-        bool s = valid && (all || keys[i] > T);
-        if (valid && !all && keys[i] == T) {
-            run += wts[i];
-            s = run <= remaining;
-        }
-        sel[i] = s;
-        cnt += s ? 1 : 0;
-    }
-    int total;
-    int pos = block_scan_incl<NT>(cnt, sh, &total) - cnt;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        if (sel[i]) {
-            if (pos < dst_cap) dst[pos] = base + i;
-            ++pos;
-        }
-    }
-    (void)lane;
+    const int total = radix_select_prefix_emit<NT, PER>(keys, wts, base, n, budget, [&](int pos, int idx, int) {
+        if (pos < dst_cap) dst[pos] = idx;
+    }, sh);
     return min(total, dst_cap);
 }
 

@@ -7,61 +7,38 @@
 // int(pages * ratio)) with forced first / last pages).  Variable chunks fill a
 // token budget with the longest prefix of the score order that fits.
 //
-// All three budgets are one weighted radix select (radix_select.h): weight 1
-// per chunk for chunk budgets, the chunk length for token budgets.  Forced
-// pages get the key 0xffffffff, above every finite score, so they are always
-// part of the prefix and count inside K.  One workgroup per row (256 threads
-// up to 2048 chunks, else 1024), 8 consecutive candidates per thread in
-// registers (up to 8192 chunks).
-#include "bsa_internal.h"
+// All three budgets are one weighted radix select (radix_select.h) over the
+// keys of select_rules.h: weight 1 per chunk for chunk budgets, the chunk
+// length for token budgets.  One workgroup of 1024 threads per row, 2
+// consecutive candidates per thread up to 2048 chunks, else 8 (up to 8192):
+// the selection is a chain of short dependent steps, and 16 waves keep every
+// SIMD busy while one waits.  The scores are requested before the row length
+// is known (clamped into the row) so the two loads overlap.
 #include "radix_select.h"
+#include "select_rules.h"
 
 namespace bsa {
 
-constexpr int kSelPer = 8;
-
-template <int NT>
+template <int NT, int PER>
 __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ scores, KvView kv, ChunkView ch,
                                                         bsa_budget bud, int32_t *__restrict__ sel_idx,
                                                         int32_t *__restrict__ sel_count, int max_sel) {
     __shared__ RadixShared sh;
     const int h = blockIdx.x, b = blockIdx.y;
+    const float *row = scores + ((int64_t)b * kv.hkv + h) * ch.max_chunks;
+    const int base = threadIdx.x * PER;
+    float raw[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) raw[i] = row[min(base + i, ch.max_chunks - 1)];
     const int L = kv.seq_lens[b];
     const int n = ch.starts ? ch.num[b] : (L + kv.page - 1) >> kv.log2page;
-    const float *row = scores + ((int64_t)b * kv.hkv + h) * ch.max_chunks;
-    int64_t budget;
-    bool forced_bos = false, forced_eos = false;
-    const bool tokens = bud.mode == BSA_BUDGET_TOKENS;
-    if (bud.mode == BSA_BUDGET_TOPK) {
-        budget = bud.top_k;
-    } else if (tokens) {
-        budget = bud.tokens;
-    } else {
-        int64_t K = (int64_t)floor((double)n * bud.ratio);
-        K = max(K, (int64_t)(1 + (bud.bos ? 1 : 0) + (bud.eos ? 1 : 0)));
-        K = min(K, (int64_t)n);
-        budget = K;
-        forced_bos = bud.bos != 0;
-        forced_eos = bud.eos != 0;
-    }
-    const int base = threadIdx.x * kSelPer;
-    uint32_t keys[kSelPer];
-    int wts[kSelPer];
-    const int32_t *st = ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr;
-#pragma unroll
-    for (int i = 0; i < kSelPer; ++i) {
-        const int c = base + i;
-        keys[i] = 0u;
-        wts[i] = 1;
-        if (c < n) {
-            uint32_t k = float_key(row[c]);
-            if ((forced_bos && c == 0) || (forced_eos && c == n - 1)) k = 0xffffffffu;
-            keys[i] = k;
-            if (tokens) wts[i] = st ? st[c + 1] - st[c] : min(kv.page, L - (c << kv.log2page));
-        }
-    }
+    const RowBudget rb = row_budget(bud, n);
+    uint32_t keys[PER];
+    int wts[PER];
+    select_keys<PER>(raw, base, n, rb, ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr, L,
+                         kv.page, kv.log2page, keys, wts);
     int32_t *dst = sel_idx + ((int64_t)b * kv.hkv + h) * max_sel;
-    const int cnt = radix_select_prefix<NT, kSelPer>(keys, wts, base, n, budget, dst, max_sel, sh);
+    const int cnt = radix_select_prefix<NT, PER>(keys, wts, base, n, rb.budget, dst, max_sel, sh);
     for (int i = cnt + threadIdx.x; i < max_sel; i += NT) dst[i] = -1;
     if (threadIdx.x == 0) sel_count[(int64_t)b * kv.hkv + h] = cnt;
 }
@@ -69,10 +46,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ sc
 hipError_t launch_select(const float *scores, const KvView &kv, const ChunkView &ch, const bsa_budget &b,
                          int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, hipStream_t s) {
     dim3 grid(kv.hkv, kv.batch);
-    if (ch.max_chunks <= 256 * kSelPer)
-        hipLaunchKernelGGL(select_kernel<256>, grid, dim3(256), 0, s, scores, kv, ch, b, sel_idx, sel_count, max_sel);
+    if (ch.max_chunks <= 1024 * 2)
+        hipLaunchKernelGGL((select_kernel<1024, 2>), grid, dim3(1024), 0, s, scores, kv, ch, b, sel_idx, sel_count,
+                           max_sel);
     else
-        hipLaunchKernelGGL(select_kernel<1024>, grid, dim3(1024), 0, s, scores, kv, ch, b, sel_idx, sel_count,
+        hipLaunchKernelGGL((select_kernel<1024, 8>), grid, dim3(1024), 0, s, scores, kv, ch, b, sel_idx, sel_count,
                            max_sel);
     return hipGetLastError();
 }

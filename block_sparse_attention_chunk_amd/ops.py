@@ -51,7 +51,8 @@ def _dtype_code(t: torch.Tensor) -> int:
 class KVCache:
     """A paged K/V cache in device memory.
 
-    paged layout:       k, v [n_pages][H_kv][page_size][D], block_table [B][max_pages]
+    paged layout:       k, v [n_pages][H_kv][page_size][D] (any strides, the
+                        same for both), block_table [B][max_pages]
     token-major layout: k, v [T][H_kv][D] in blocks of page_size tokens (batch 1,
                         block_table None)
     """
@@ -65,17 +66,24 @@ class KVCache:
 
     def __post_init__(self):
         k = self.k
+        # element strides are taken from the tensors, so K and V may be views
+        # into one buffer (e.g. [n_pages][H_kv][2][page_size][D], K and V of a
+        # page next to each other); both must share them
+        if self.v is not None and tuple(self.v.stride()) != tuple(k.stride()):
+            raise ValueError("k and v must have the same strides")
+        if k.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
         if self.token_major:
             T, H, D = k.shape
             self.num_kv_heads, self.head_dim = H, D
-            self.strides = (self.page_size * H * D, D, H * D)
+            self.strides = (self.page_size * k.stride(0), k.stride(1), k.stride(0))
             if self.max_pages is None:
                 self.max_pages = (T + self.page_size - 1) // self.page_size
         else:
             _, H, P, D = k.shape
             assert P == self.page_size
             self.num_kv_heads, self.head_dim = H, D
-            self.strides = (H * P * D, P * D, D)
+            self.strides = (k.stride(0), k.stride(1), k.stride(2))
             if self.max_pages is None:
                 self.max_pages = int(self.block_table.shape[1])
         self.batch = int(self.seq_lens.shape[0])
@@ -252,12 +260,15 @@ def sparse_attn_decode(q: torch.Tensor, kv: KVCache, sel_idx: Optional[torch.Ten
                        sel_count: Optional[torch.Tensor] = None, chunks: Optional[Chunks] = None,
                        scale: Optional[float] = None, num_splits: int = 0, out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """bsa_sparse_attn_decode: q [B][H_q][D] -> out [B][H_q][D] float32; sel_idx None = dense."""
+    """bsa_sparse_attn_decode: q [B][H_q][D] -> out [B][H_q][D] float32; sel_idx None = dense.
+    out=PARTIALS leaves the split partials in the workspace (see decode_merge)."""
     B, Hq, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    elif out is PARTIALS:
+        out = None
     max_sel = 0 if sel_idx is None else int(sel_idx.shape[2])
     items = max_sel if sel_idx is not None else _max_chunks(kv, chunks)
     need = decode_workspace_bytes(kv, Hq, items, num_splits)
@@ -269,6 +280,48 @@ def sparse_attn_decode(q: torch.Tensor, kv: KVCache, sel_idx: Optional[torch.Ten
                                   _ptr(sel_count), max_sel, float(scale), num_splits, _ptr(out), _ptr(workspace),
                                   ws_bytes, _stream(q.device))
     _abi.check(rc, "bsa_sparse_attn_decode")
+    return out
+
+
+PARTIALS = object()   # out=PARTIALS: skip the split merge, keep the partials in the workspace
+
+
+def decode_merge(workspace: torch.Tensor, batch: int, num_q_heads: int, head_dim: int, num_splits: int,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bsa_decode_merge: the split partials in `workspace` -> out [B][H_q][D] float32."""
+    if out is None:
+        out = torch.empty((batch, num_q_heads, head_dim), dtype=torch.float32, device=workspace.device)
+    rc = _abi.lib().bsa_decode_merge(_ptr(workspace), batch, num_q_heads, head_dim, num_splits, _ptr(out),
+                                     _stream(workspace.device))
+    _abi.check(rc, "bsa_decode_merge")
+    return out
+
+
+def select_attn_decode(q: torch.Tensor, kv: KVCache, scores: torch.Tensor, budget: Budget,
+                       scale: Optional[float] = None, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, sel_idx: Optional[torch.Tensor] = None,
+                       sel_count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bsa_select_attn_decode: selection + attention in one launch (16-token
+    pages).  q [B][H_q][D], scores [B][H_kv][max_pages] -> out [B][H_q][D]
+    float32; sel_idx / sel_count, when given, receive the kept list."""
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    elif out is PARTIALS:
+        out = None
+    K = budget.max_selected(kv.max_pages)
+    need = decode_workspace_bytes(kv, Hq, K, num_splits)
+    if workspace is None and need:
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    max_sel = 0 if sel_idx is None else int(sel_idx.shape[2])
+    L = _abi.lib()
+    rc = L.bsa_select_attn_decode(_ptr(q), Hq, ctypes.byref(kv.struct()), _ptr(scores),
+                                  ctypes.byref(budget.struct()), float(scale), num_splits, _ptr(out), _ptr(sel_idx),
+                                  _ptr(sel_count), max_sel, _ptr(workspace), ws_bytes, _stream(q.device))
+    _abi.check(rc, "bsa_select_attn_decode")
     return out
 
 

@@ -214,7 +214,9 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * Group size H_q/H_kv <= 16.  workspace >= bsa_decode_workspace_bytes(...)
  * (0 bytes when the resolved split count is 1): the split partials, merged
  * by a second kernel on the same stream.  Splits are capped at 64.  Calls that
- * share a workspace must not overlap.
+ * share a workspace must not overlap.  sel_count entries must not exceed
+ * max_sel.  With more than one split, out may be NULL: the merge is skipped
+ * and the workspace holds the partials (layout at bsa_decode_merge).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
  */
 int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits);
@@ -222,6 +224,42 @@ size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t
 int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_chunks *chunks,
                            const int32_t *sel_idx, const int32_t *sel_count, int32_t max_sel, float softmax_scale,
                            int32_t num_splits, float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The split merge of step 4 on its own, for partials left in the workspace by
+ * bsa_sparse_attn_decode / bsa_select_attn_decode with out == NULL.  The
+ * workspace holds o [batch][H_q][num_splits][head_dim] float32 (unnormalised
+ * per-split outputs) followed by (m, l) [batch][H_q][num_splits][2] float32
+ * (per-split running max of the base-2 scaled logits and softmax sum);
+ *   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+ * num_splits in [2, 64]; head_dim 64 or 128.  out [batch][H_q][head_dim].
+ * Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ */
+int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                     int32_t num_splits, float *out, void *stream);
+
+/*
+ * Steps 3 + 4 fused (decode, [P1] "The comparison": keep the top chunks under
+ * the budget, attend only to them; [P2] ratio budget): the selection of
+ * bsa_select_topk and the attention of bsa_sparse_attn_decode in one launch
+ * (plus the split merge), for fixed 16-token pages without a chunk list.
+ * scores [batch][H_kv][max_pages] from bsa_score_chunks.  The kept set is the
+ * one bsa_select_topk returns for the same scores and budget, and out is
+ * bit-identical to bsa_sparse_attn_decode on that set with the same split
+ * count.  sel_idx / sel_count (both or neither) optionally receive the kept
+ * list as bsa_select_topk writes it (max_sel >= the largest possible
+ * selection K).  Splits resolve as bsa_decode_num_splits(kv, H_q, K,
+ * num_splits), num_splits in [0, 64], and each split keeps at most 2048
+ * pages; workspace >= bsa_decode_workspace_bytes(kv, H_q, K, num_splits).
+ * max_pages <= 8192; group size <= 16.  Calls sharing a workspace must not
+ * overlap.  out may be NULL with more than one split, as for
+ * bsa_sparse_attn_decode.
+ * Errors: INVALID_ARG, UNSUPPORTED (page size, limits), WORKSPACE, LAUNCH.
+ */
+int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
+                           const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
+                           int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * Step 5 attention ([P3] step 5): causal prefill over query tiles of

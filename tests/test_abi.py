@@ -168,3 +168,46 @@ def test_tile_prefill_argument_checks():
     assert call(kvt, stride=0) == _abi.BSA_ERR_INVALID_ARG
     assert call(_kv(page_size=64, stride_page=64 * 2 * 128, stride_head=128, stride_token=256, block_table=None,
                     dtype=_abi.BSA_F32, head_dim=128)) == _abi.BSA_ERR_UNSUPPORTED
+
+
+def test_fused_select_decode_argument_checks():
+    L = _abi.lib()
+    B = _abi.bsa_budget
+    top = B(_abi.BSA_BUDGET_TOPK, 8, 0, 0, 0, 0.0)
+
+    def call(kv=None, hq=8, budget=top, splits=0, sel=False, cnt=False, max_sel=0, ws=None, wsb=0, scale=0.088):
+        kv = kv or _kv()
+        return L.bsa_select_attn_decode(FAKE, hq, ctypes.byref(kv), FAKE, ctypes.byref(budget), scale, splits, FAKE,
+                                        FAKE if sel else None, FAKE if cnt else None, max_sel, ws, wsb, None)
+
+    assert call(kv=_kv(page_size=32)) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(kv=_kv(max_pages=9000)) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(hq=34) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(sel=True) == _abi.BSA_ERR_INVALID_ARG                    # sel_idx without sel_count
+    assert call(sel=True, cnt=True, max_sel=7) == _abi.BSA_ERR_INVALID_ARG  # 8 pages may be kept
+    assert call(splits=65) == _abi.BSA_ERR_INVALID_ARG
+    assert call(scale=-1.0) == _abi.BSA_ERR_INVALID_ARG
+    assert call(budget=B(_abi.BSA_BUDGET_RATIO, 0, 0, 1, 1, 0.0)) == _abi.BSA_ERR_INVALID_ARG
+    # 4096 pages in one split exceed the 2048 kept per split
+    big = _kv(max_pages=4096)
+    assert call(kv=big, budget=B(_abi.BSA_BUDGET_TOPK, 4096, 0, 0, 0, 0.0), splits=1) == _abi.BSA_ERR_INVALID_ARG
+    assert "splits" in L.bsa_last_error().decode()
+    # automatic splits respect that limit
+    assert L.bsa_decode_num_splits(ctypes.byref(_kv(batch=64, num_kv_heads=8, max_pages=8192)), 64, 8192, 0) >= 4
+    need = L.bsa_decode_workspace_bytes(ctypes.byref(_kv()), 8, 8, 4)
+    assert need == 1 * 8 * 4 * 130 * 4
+    assert call(splits=4) == _abi.BSA_ERR_WORKSPACE
+    assert call(splits=4, ws=FAKE, wsb=need - 1) == _abi.BSA_ERR_WORKSPACE
+
+
+def test_merge_and_partials_argument_checks():
+    L = _abi.lib()
+    assert L.bsa_decode_merge(None, 1, 8, 128, 4, FAKE, None) == _abi.BSA_ERR_INVALID_ARG
+    assert L.bsa_decode_merge(FAKE, 1, 8, 96, 4, FAKE, None) == _abi.BSA_ERR_UNSUPPORTED
+    assert L.bsa_decode_merge(FAKE, 1, 8, 128, 1, FAKE, None) == _abi.BSA_ERR_INVALID_ARG
+    assert L.bsa_decode_merge(FAKE, 1, 8, 128, 65, FAKE, None) == _abi.BSA_ERR_INVALID_ARG
+    assert L.bsa_decode_merge(FAKE, 0, 8, 128, 4, FAKE, None) == _abi.BSA_ERR_INVALID_ARG
+    # out == NULL needs more than one split
+    kv = _kv()
+    rc = L.bsa_sparse_attn_decode(FAKE, 8, ctypes.byref(kv), None, FAKE, FAKE, 8, 0.088, 1, None, None, 0, None)
+    assert rc == _abi.BSA_ERR_INVALID_ARG and "out may be NULL" in L.bsa_last_error().decode()

@@ -1,5 +1,6 @@
 """GPU-vs-oracle parity of the decode path (metadata, scores, selection,
-split-K attention, dense baseline) through the C ABI.
+split-K attention, dense baseline, fused selection + attention) through the
+C ABI.
 
 Workloads: the tiny fp32 decode; the 32:4-head, d 128 replay-shaped decode at
 29,504 tokens (budgets 4096 / 8192, envelope and centroid); the same with
@@ -47,7 +48,18 @@ def run_decode_case(case, dev, kind, budget, forced=(), splits=(0,), check_dense
     sel, cnt = ops.select_topk(scores, kv, budget, chunks)
     outs = {s: ops.sparse_attn_decode(q, kv, sel, cnt, chunks, num_splits=s) for s in splits}
     dense = ops.sparse_attn_decode(q, kv, None, None, chunks) if check_dense else None
+    # the fused selection + attention (16-token pages): same kept set, and the
+    # same output bits as the two calls at the same split count
+    fused = {}
+    if chunks is None and case.page_size == 16:
+        for s in splits:
+            fsel, fcnt = torch.full_like(sel, -7), torch.full_like(cnt, -7)
+            fout = ops.select_attn_decode(q, kv, scores, budget, num_splits=s, sel_idx=fsel, sel_count=fcnt)
+            fused[s] = (fout, fsel, fcnt)
     torch.cuda.synchronize()
+    for s, (fout, fsel, fcnt) in fused.items():
+        assert torch.equal(fsel, sel) and torch.equal(fcnt, cnt), f"fused selection differs (splits={s})"
+        assert torch.equal(fout, outs[s]), f"fused output not bit-identical (splits={s})"
     kmin, kmax, cen = _np(meta.kmin), _np(meta.kmax), _np(meta.centroid)
     scores, sel, cnt = _np(scores), _np(sel), _np(cnt)
 
@@ -88,7 +100,7 @@ def run_decode_case(case, dev, kind, budget, forced=(), splits=(0,), check_dense
         derr = max_abs(_np(dense), dref)
         assert derr <= tol, f"dense max-abs {derr:.3g}"
     log(f"  ok: worst score err {worst:.2e} D, in-band selection diffs {diffs}, attn err "
-        f"{max(max_abs(_np(o), ref) for o in outs.values()):.2e}")
+        f"{max(max_abs(_np(o), ref) for o in outs.values()):.2e}, fused checked: {bool(fused)}")
     return {"sel": sel, "cnt": cnt, "out": _np(next(iter(outs.values()))), "ref": ref, "osel": osel, "ocnt": ocnt}
 
 
@@ -203,3 +215,41 @@ def test_batched_ratio_full_size(dev, ratio):
     case = synth.batched_decode()
     run_decode_case(case, dev, ops.BSA_CENTROID, ops.Budget.ratio_budget(ratio, 1, 1), forced=("bos", "eos"),
                     check_dense=ratio == 0.125)
+
+
+def test_partials_then_merge_matches_one_call(dev):
+    """out == NULL leaves the split partials in the workspace; bsa_decode_merge
+    on them gives the same bits as the single call (unfused and fused)."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.batched_decode(cid=15, batch=3, lo=1500, hi=4000)
+    kv, _ = gpu_kv(case, dev)
+    q = ops.upload(case.q, dev)
+    meta = ops.build_chunk_meta(kv)
+    sc = ops.score_chunks(q, kv, meta, ops.BSA_CENTROID)
+    bud = ops.Budget.ratio_budget(0.25, 1, 1)
+    sel, cnt = ops.select_topk(sc, kv, bud)
+    B, Hq, D = case.batch, case.num_q_heads, case.head_dim
+    for splits in (2, 5, 64):
+        ws = torch.zeros((ops.decode_workspace_bytes(kv, Hq, int(sel.shape[2]), splits),), dtype=torch.uint8,
+                         device=dev)
+        full = ops.sparse_attn_decode(q, kv, sel, cnt, num_splits=splits)
+        ops.sparse_attn_decode(q, kv, sel, cnt, num_splits=splits, out=ops.PARTIALS, workspace=ws)
+        merged = ops.decode_merge(ws, B, Hq, D, splits)
+        ws.zero_()
+        ops.select_attn_decode(q, kv, sc, bud, num_splits=splits, out=ops.PARTIALS, workspace=ws)
+        fmerged = ops.decode_merge(ws, B, Hq, D, splits)
+        torch.cuda.synchronize()
+        assert torch.equal(full, merged), splits
+        assert torch.equal(full, fmerged), splits
+    ref = oracle.decode_attn(case.q, oracle_cache(case), _np(sel), _np(cnt))
+    assert max_abs(_np(full), ref) <= ATTN_ABS["bf16"]
+
+
+def test_fused_token_budget_fixed_pages(dev):
+    """Token budget over fixed pages (last page shorter) through the fused
+    entry point: kept set equals the oracle's on the same scores."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(16, batch=3, seq_lens=[1000, 2049, 4100], num_q_heads=32, num_kv_heads=4,
+                             head_dim=128, name="tokens-fixed")
+    run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.token_budget(1000), band_exact_count=False,
+                    splits=(0, 3), check_dense=False)
