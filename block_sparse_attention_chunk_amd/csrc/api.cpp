@@ -366,8 +366,11 @@ int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num
         return fail(BSA_ERR_UNSUPPORTED, "tile prefill needs batch 1 and a token-major cache (block_table NULL)");
     if (tile_rows != 64 || kv->page_size != 64)
         return fail(BSA_ERR_UNSUPPORTED, "tile prefill supports 64-row tiles over 64-token blocks");
+    if (kv->stride_page != 64 * kv->stride_token)
+        return fail(BSA_ERR_UNSUPPORTED, "tile prefill needs a token-major cache (stride_page == 64 * stride_token)");
     if (num_rows < 1) return fail(BSA_ERR_INVALID_ARG, "num_rows must be >= 1");
     if (kv_idx && idx_stride < 1) return fail(BSA_ERR_INVALID_ARG, "idx_stride must be >= 1");
+    if (kv_idx && idx_stride > 1024) return fail(BSA_ERR_UNSUPPORTED, "idx_stride %d exceeds 1024", idx_stride);
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
         return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
     return launched(bsa::launch_tile_prefill(q, num_q_heads, num_rows, v, tile_rows, kv_idx, idx_stride,

@@ -8,18 +8,32 @@
 // sentinel, so an untriggered tile costs its k blocks only.
 //
 // One workgroup per (tile, KV head, row half): one wave per query head of the
-// GQA group, 32 rows per wave (two 16-row MFMA column tiles).  For each
-// selected 64-key block the workgroup stages K (bf16, row-major) and V
-// (converted to fp16, transposed to [dim][key]) in LDS once for all heads.
-// Per 32-key half:
-//   S^T[key][row] = K . Q^T            v_mfma_f32_16x16x32_bf16, Q^T in VGPRs
-//   online softmax per row (fp32, log2 domain; the row is the MFMA column, so
-//   its 8 keys per lane reduce with two cross-lane maxes)
-//   O^T[dim][row] += V^T . P^T         v_mfma_f32_16x16x32_f16
-// P^T is built straight from the S^T accumulators of two 16-key tiles; V^T
-// uses the same per-lane key order, so the products pair up regardless of
-// the instruction's internal k order.  bf16 -> fp16 is exact for |v| in the
-// fp16 normal range.  Keys after a row are masked only in the diagonal block.
+// GQA group, 32 rows per wave (two 16-row MFMA column tiles), so each staged
+// K/V block feeds G x 32 query rows.  Per selected 64-key block:
+//   S^T[key][row] = K . Q^T      16 v_mfma_f32_16x16x32_bf16 per row tile,
+//                                Q^T in VGPRs, K rows read from LDS in a
+//                                permuted order (below)
+//   online softmax once per block per row (fp32, log2 domain); the row is the
+//   MFMA column, so its 16 keys per lane reduce with two cross-lane maxes
+//   O^T[dim][row] += V^T . P^T   16 v_mfma_f32_16x16x32_f16 per row tile
+// K tile kt (16 keys) of 32-key chunk c holds, in MFMA row 4a + i, the key
+// 32c + 8a + 4(kt & 1) + i.  The S^T accumulator of lane (row, a) then holds
+// keys 32c + 8a .. 32c + 8a + 7 across the chunk's two tiles, which is exactly
+// the 8-key slice of P^T that lane supplies to the P.V product.
+//
+// Staging: K and V blocks are copied straight from global memory into LDS
+// (global_load_lds, 16 bytes a lane, 1 KiB = 4 rows of 256 bytes per wave
+// instruction), three blocks deep, so no staging registers are needed and
+// block b+2 is in flight while block b is computed.  Inside a row the 16-byte
+// chunk c is stored at position c ^ swz(row), swz taking row bits 0-1 and 3-4:
+// the 16 rows one MFMA operand read touches then hit 16 different chunk
+// positions (no bank conflicts).  V is converted bf16 -> fp16 in place by all
+// threads once its block has landed, and the V^T operand (8 keys of one dim
+// per lane) comes from row-major V with two ds_read_b64_tr_b16 (4 keys each).
+// P is rounded to fp16 and the row sums are taken from the rounded values on
+// the matrix cores (an all-ones A operand); bf16 -> fp16 is exact for |v| in
+// the fp16 normal range.  Keys after a row are masked
+// only in the diagonal block.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -27,139 +41,298 @@ namespace bsa {
 constexpr int kPfD = 128;
 constexpr int kPfBlock = 64;
 constexpr int kPfRowsPerWave = 32;
-constexpr int kKStride = kPfD + 8;      // bf16 elements per staged K row (+16 B)
-constexpr int kVStride = kPfBlock + 8;  // fp16 elements per staged V^T row (+16 B)
+constexpr int kPfRowBytes = kPfD * 2;                 // 256 bytes per staged row
+constexpr int kPfBlockBytes = kPfBlock * kPfRowBytes;  // 16 KiB for K or V
+constexpr int kPfStageBytes = 2 * kPfBlockBytes;       // K then V
+constexpr int kPfStages = 3;
+constexpr int kPfMaxList = 1024;                       // selected blocks per (tile, KV head) held in LDS
+constexpr int kPfInstrs = kPfStageBytes / 1024;        // 1 KiB wave instructions per block
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_raw lds_f16x4_t;
 
-__global__ __launch_bounds__(512) void tile_prefill_kernel(const uint16_t *__restrict__ q, int hq, int rows,
-                                                           KvView kv, const int32_t *__restrict__ kv_idx,
-                                                           int idx_stride, float scale_log2,
-                                                           float *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kPfBlock * kKStride];
-    __shared__ __attribute__((aligned(16))) _Float16 vt[kPfD * kVStride];
+__device__ __forceinline__ int pf_swz(int row) { return (row & 3) | ((row >> 1) & 12); }
+
+// byte offset of (row, 16-byte chunk) inside a staged K or V block
+__device__ __forceinline__ int pf_off(int row, int chunk) { return row * kPfRowBytes + 16 * (chunk ^ pf_swz(row)); }
+
+// s_waitcnt vmcnt(n) alone (expcnt / lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt lgkmcnt(0) alone
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Workgroup barrier for the staging pipeline.  __syncthreads() would also wait
+// for this wave's copies still in flight to a different buffer (vmcnt(0));
+// here every wave has already waited for exactly what the next phase reads
+// (its own copies, vmcnt; its LDS reads and writes, lgkmcnt), and the empty
+// asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// LDS byte address of a __shared__ pointer
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One 16-byte-per-lane copy global -> LDS (lane l to lds + 16 l).  Written as
+// an opaque statement: the compiler does not track it, so it adds no wait of
+// its own before later LDS reads of other buffers; the kernel waits for these
+// copies explicitly (vmcnt) before the barrier that publishes a buffer.  It
+// writes no register, and the compiler's own counter waits only get stricter.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+// Issue this wave's share of one block's copy into stage `buf` (lds byte
+// address): wave instruction u (u < 16: K rows 4u..4u+3, else V rows), lane
+// l writes row 4(u mod 16) + l/16 at chunk position l mod 16, so it loads
+// chunk (l mod 16) ^ swz(row).  Rows past the end clamp onto the last row
+// (those keys are masked).  Every wave issues the same count.  The cache is
+// token-major: token pos of a head starts at base + pos * row_bytes.
+template <int G>
+__device__ __forceinline__ void issue_block(char *lds_stage, const uint16_t *kbase, const uint16_t *vbase,
+                                            int64_t row_bytes, int blk, int rows, int w, int lane) {
+    constexpr int NI = (kPfInstrs + G - 1) / G;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int u = min(w + G * i, kPfInstrs - 1);  // duplicates rewrite identical bytes
+        const int row = 4 * (u & 15) + (lane >> 4);
+        const int chunk = (lane & 15) ^ pf_swz(row);
+        const int pos = min(blk * kPfBlock + row, rows - 1);
+        const char *src = reinterpret_cast<const char *>(u < 16 ? kbase : vbase) + pos * row_bytes + chunk * 16;
+        dma16(src, lds_addr(lds_stage) + u * 1024);
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__restrict__ q, int hq, int rows,
+                                                              KvView kv, const int32_t *__restrict__ kv_idx,
+                                                              int idx_stride, float scale_log2,
+                                                              float *__restrict__ out) {
+    constexpr int NT = 64 * G;
+    constexpr int NI = (kPfInstrs + G - 1) / G;
+    // three distinct LDS objects (not one array): each unrolled step names its
+    // buffers statically, so the compiler can tell that the copy in flight
+    // never aliases the buffer being read and adds no wait for it
+    __shared__ __attribute__((aligned(1024))) char stage0[kPfStageBytes];
+    __shared__ __attribute__((aligned(1024))) char stage1[kPfStageBytes];
+    __shared__ __attribute__((aligned(1024))) char stage2[kPfStageBytes];
+    __shared__ int blist[kPfMaxList];
+    __shared__ int nblk_s;
     const int t = blockIdx.x >> 1, half = blockIdx.x & 1, h = blockIdx.y;
-    const int g = hq / kv.hkv;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, G = lane >> 4;
-    const int nthreads = blockDim.x;
-    const int j = h * g + w;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n16 = lane & 15, G4 = lane >> 4;
+    const int j = h * G + w;
     const int rbase = t * kPfBlock + half * kPfRowsPerWave;
     const uint16_t *kbase = reinterpret_cast<const uint16_t *>(kv.k) + (int64_t)h * kv.sh;
     const uint16_t *vbase = reinterpret_cast<const uint16_t *>(kv.v) + (int64_t)h * kv.sh;
+    const int64_t row_bytes = kv.st * 2;  // token-major: stride_page == 64 * stride_token (host-checked)
 
-    // Q^T operand: rows rbase + 16*rt + n16, dims 32s + 8G .. +8
+    // the visible selected blocks: a prefix of the ascending, -1 padded row
+    // (idx_stride <= kPfMaxList, host-checked); dense: blocks 0 .. t
+    const int32_t *idx = kv_idx ? kv_idx + ((int64_t)t * kv.hkv + h) * idx_stride : nullptr;
+    if (threadIdx.x == 0) nblk_s = idx ? idx_stride : t + 1;
+    __syncthreads();
+    if (idx) {
+        for (int i = threadIdx.x; i < idx_stride; i += NT) {
+            const int blk = idx[i];
+            blist[i] = blk;
+            if (blk < 0 || blk > t) atomicMin(&nblk_s, i);
+        }
+    }
+    // Q^T operand: rows rbase + 16*rt + n16, dims 32s + 8*G4 .. +8
     bf16x8 qb[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        const int r = rbase + 16 * rt + n16;
+        const int r = min(rbase + 16 * rt + n16, rows - 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (r < rows) v = *reinterpret_cast<const uint4 *>(q + ((int64_t)r * hq + j) * kPfD + 32 * s + 8 * G);
-            qb[rt][s] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int s = 0; s < 4; ++s)
+            qb[rt][s] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(q + ((int64_t)r * hq + j) * kPfD + 32 * s + 8 * G4));
     }
     f32x4 o[8][2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-    const int32_t *idx = kv_idx ? kv_idx + ((int64_t)t * kv.hkv + h) * idx_stride : nullptr;
-    const int nsel = kv_idx ? idx_stride : t + 1;
-    for (int ii = 0; ii < nsel; ++ii) {
-        const int blk = idx ? idx[ii] : ii;
-        if (blk < 0) break;  // sentinels are trailing
-        if (blk > t) continue;  // a block after the diagonal holds no visible key
-        __syncthreads();     // previous block's LDS reads are done
-        // stage K (row-major bf16) and V^T (fp16)
-        for (int c = threadIdx.x; c < kPfBlock * (kPfD / 8); c += nthreads) {
-            const int key = c >> 4, piece = c & 15;
-            const int pos = blk * kPfBlock + key;
-            uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-            if (pos < rows) {
-                const int64_t off = (int64_t)blk * kv.sp + (int64_t)key * kv.st + piece * 8;
-                kw = *reinterpret_cast<const uint4 *>(kbase + off);
-                vw = *reinterpret_cast<const uint4 *>(vbase + off);
-            }
-            *reinterpret_cast<uint4 *>(ks + key * kKStride + piece * 8) = kw;
-            const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+    float m_run[2] = {-INFINITY, -INFINITY};
+    f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const f16x8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                        (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+    __syncthreads();
+    const int nb = nblk_s;
+    auto block_at = [&](int i) { return idx ? blist[min(i, max(nb - 1, 0))] : min(i, t); };
+    auto convert_v = [&](char *buf) {  // bf16 -> fp16 in place, 8 values per 16-byte chunk
+        uint4 *v = reinterpret_cast<uint4 *>(buf + kPfBlockBytes);
+        for (int c = threadIdx.x; c < kPfBlockBytes / 16; c += NT) {
+            const uint4 x = v[c];
+            const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+            uint32_t y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                vt[(piece * 8 + 2 * e) * kVStride + key] = (_Float16)bf16_lo(vv[e]);
-                vt[(piece * 8 + 2 * e + 1) * kVStride + key] = (_Float16)bf16_hi(vv[e]);
+                const _Float16 lo = (_Float16)bf16_lo(wd[e]), hi = (_Float16)bf16_hi(wd[e]);
+                y[e] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
             }
+            v[c] = make_uint4(y[0], y[1], y[2], y[3]);
         }
-        __syncthreads();
+    };
+
+    // prologue: blocks 0 and 1 copied, block 0 converted.  Everything this
+    // wave loaded so far (Q included) is waited for here, so the compiler,
+    // which does not see the copies, needs no wait of its own in the loop.
+    if (nb > 0) {
+        issue_block<G>(stage0, kbase, vbase, row_bytes, block_at(0), rows, w, lane);
+        issue_block<G>(stage1, kbase, vbase, row_bytes, block_at(1), rows, w, lane);
+    }
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    stage_barrier();
+    if (nb > 0) convert_v(stage0);
+    wait_lgkm0();
+    stage_barrier();
+    // Per-lane LDS byte offsets, the same for every block.  The K row of MFMA
+    // row n16 in tile kt is 32(kt>>1) + 4(kt&1) + krow_lo, whose swizzle is
+    // n16 whatever kt is, so chunk 4st + G4 sits at 4(st ^ (n16>>2)) +
+    // (G4 ^ (n16&3)).  The V rows read by lane (n16, G4) are
+    // 32c + 8G4 + 4hh + (n16>>2), swizzle (n16>>2) | (G4<<2) whatever c and hh
+    // are; the lane's 8-byte piece of dims 16dt + 4(n16&3) is chunk
+    // 2dt + ((n16>>1)&1), half n16&1.
+    const int krow_lo = 8 * (n16 >> 2) + (n16 & 3);
+    int koff[4], voff[8];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) koff[st] = krow_lo * kPfRowBytes + 16 * (4 * (st ^ (n16 >> 2)) + (G4 ^ (n16 & 3)));
+    {
+        const int vswz = (n16 >> 2) | (G4 << 2);
+        const int vrow = 8 * G4 + (n16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            voff[dt] = vrow * kPfRowBytes + 16 * ((2 * dt + ((n16 >> 1) & 1)) ^ vswz) + 8 * (n16 & 1);
+    }
+    // one block: bcur holds block ii (converted), bn1 receives block ii+1 (in
+    // flight), bn2 block ii+2 (issued here; last read two blocks ago)
+    auto step = [&](int ii, char *bcur, char *bn1, char *bn2) {
+        const int blk = block_at(ii);
+        issue_block<G>(bn2, kbase, vbase, row_bytes, block_at(ii + 2), rows, w, lane);
+        const char *kc = bcur;
+        const char *vc = bcur + kPfBlockBytes;
         const bool diag = blk == t;
+        // S^T for the 64 keys: 4 key tiles x 2 row tiles
+        f32x4 s[4][2];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            f32x4 s[2][2];  // [key tile][row tile]
+        for (int kt = 0; kt < 4; ++kt) {
+            const int key0 = 32 * (kt >> 1) + 4 * (kt & 1);  // + krow_lo (in koff)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int rt = 0; rt < 2; ++rt) s[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) s[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + (32 * kh + 16 * kt + n16) * kKStride +
-                                                                        32 * st + 8 * G);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-                        s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][st], s[kt][rt], 0, 0, 0);
-                }
-            }
-            f16x8 pb[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int r = rbase + 16 * rt + n16;
-                float x[2][4];
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int pos = blk * kPfBlock + 32 * kh + 16 * kt + 4 * G + i;
-                        const bool ok = pos < rows && (!diag || pos <= r);
-                        x[kt][i] = ok ? s[kt][rt][i] * scale_log2 : -INFINITY;
-                        mx = fmaxf(mx, x[kt][i]);
-                    }
-                mx = wave_max_xor(mx, 16);
-                mx = wave_max_xor(mx, 32);
-                const float m_new = fmaxf(m_run[rt], mx);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = exp2f(m_run[rt] - m_use);
-                float psum = 0.f;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const _Float16 p = (_Float16)exp2f(x[kt][i] - m_use);
-                        psum += (float)p;  // normalise with the same rounded weights
-                        pb[rt][4 * kt + i] = p;
-                    }
-                l_run[rt] = l_run[rt] * alpha + psum;
-                m_run[rt] = m_new;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[dt][rt] *= alpha;
-            }
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const _Float16 *vrow = vt + (16 * dt + n16) * kVStride + 32 * kh + 4 * G;
-                const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow);
-                const f16x4 hi = *reinterpret_cast<const f16x4 *>(vrow + 16);
-                const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            for (int st = 0; st < 4; ++st) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kc + key0 * kPfRowBytes + koff[st]);
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
-                    o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[rt], o[dt][rt], 0, 0, 0);
+                    s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][st], s[kt][rt], 0, 0, 0);
             }
+            // bounds the operand reads in flight (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // online softmax, one step per block and row.  Masks only where a key
+        // can be invisible (the diagonal block, the ragged last block); the
+        // scale is folded into the exponent's FMA (max taken on raw scores,
+        // the scale being positive).
+        const bool need_mask = diag || (blk + 1) * kPfBlock > rows;
+        f16x8 pb[2][2];  // [key chunk][row tile]
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            if (need_mask) {
+                const int r = rbase + 16 * rt + n16;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int pos = blk * kPfBlock + 32 * (kt >> 1) + 8 * G4 + 4 * (kt & 1) + i;
+                        if (!(pos < rows && (!diag || pos <= r))) s[kt][rt][i] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][rt][i]);
+            mx = wave_max_xor(mx, 16);
+            mx = wave_max_xor(mx, 32);
+            // Lazy rescale: the reference max moves only when a row's max
+            // exceeds it by more than 2^8 (weights stay <= 256, well inside
+            // fp16), so most blocks skip rescaling the accumulators; the sums
+            // use the same reference, so the result is exact.
+            const float mb = mx * scale_log2;
+            const bool grow = mb > m_run[rt] + 8.f;
+            if (__ballot(grow)) {
+                const float m_new = grow ? mb : m_run[rt];
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);  // 0 from -inf
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[dt][rt] *= alpha;
+                lsum[rt] *= alpha;
+                m_run[rt] = m_new;
+            }
+            const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pb[kt >> 1][rt][4 * (kt & 1) + i] =
+                        (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kt][rt][i], scale_log2, -m_use));
+        }
+        // O^T += V^T . P^T over the two 32-key chunks: lane (dim 16dt + n16, G4)
+        // supplies keys 32c + 8*G4 .. +7, read as two transposed 4-key pieces
+        // (lane L of the 16-lane group points at row rb + L/4, dims 16dt + 4(L%4))
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                f16x4 pr[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const char *p = vc + (32 * c + 4 * hh) * kPfRowBytes + voff[dt];
+                    pr[hh] = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t *)p));
+                }
+                const f16x8 a = {pr[0][0], pr[0][1], pr[0][2], pr[0][3], pr[1][0], pr[1][1], pr[1][2], pr[1][3]};
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[c][rt], o[dt][rt], 0, 0, 0);
+                if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // at most 4 operand reads in flight
+            }
+            // row sums of the rounded weights: an all-ones A operand (every
+            // output row of this tile is the column sum of P^T)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+                lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[c][rt], lsum[rt], 0, 0, 0);
+        }
+        // block ii+1 has landed (only block ii+2's copies may be outstanding)
+        // and this wave's reads of bcur are done
+        wait_vmcnt<NI>();
+        wait_lgkm0();
+        stage_barrier();
+        convert_v(bn1);
+        wait_lgkm0();
+        stage_barrier();
+    };
+    for (int ii = 0; ii < nb; ii += 3) {
+        step(ii, stage0, stage1, stage2);
+        if (ii + 1 < nb) step(ii + 1, stage1, stage2, stage0);
+        if (ii + 2 < nb) step(ii + 2, stage2, stage0, stage1);
     }
-    // normalise and write: lane holds O^T[dim 16dt + 4G + i][row 16rt + n16]
+    wait_vmcnt<0>();  // no copy may still target LDS when the workgroup ends
+    // normalise and write: lane holds O^T[dim 16dt + 4*G4 + i][row 16rt + n16]
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        float l = l_run[rt] + __shfl_xor(l_run[rt], 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        const float l = lsum[rt][0];  // every row of the sum tile holds the row's total
         const int r = rbase + 16 * rt + n16;
         if (r < rows) {
             const float inv = 1.0f / l;
@@ -167,7 +340,7 @@ __global__ __launch_bounds__(512) void tile_prefill_kernel(const uint16_t *__res
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 const f32x4 v = o[dt][rt] * inv;
-                *reinterpret_cast<float4 *>(orow + 16 * dt + 4 * G) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4 *>(orow + 16 * dt + 4 * G4) = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
     }
@@ -179,8 +352,18 @@ hipError_t launch_tile_prefill(const void *q, int32_t hq, int32_t rows, const Kv
     const int g = hq / kv.hkv;
     const int n_tiles = (rows + kPfBlock - 1) / kPfBlock;
     dim3 grid(n_tiles * 2, kv.hkv), block(64 * g);
-    hipLaunchKernelGGL(tile_prefill_kernel, grid, block, 0, s, (const uint16_t *)q, hq, rows, kv, kv_idx, idx_stride,
-                       scale * kLog2e, out);
+    const float sl = scale * kLog2e;
+#define BSA_TP(G)                                                                                            \
+    case G:                                                                                                  \
+        hipLaunchKernelGGL(tile_prefill_kernel<G>, grid, block, 0, s, (const uint16_t *)q, hq, rows, kv, kv_idx, \
+                           idx_stride, sl, out);                                                             \
+        break;
+    switch (g) {
+        BSA_TP(1) BSA_TP(2) BSA_TP(3) BSA_TP(4) BSA_TP(5) BSA_TP(6) BSA_TP(7) BSA_TP(8)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef BSA_TP
     return hipGetLastError();
 }
 

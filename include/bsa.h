@@ -270,7 +270,8 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
  * baseline).  kv: batch 1, token-major bf16 [num_rows][H_kv][D] with
  * page_size == tile_rows == 64 and block_table NULL.  q [num_rows][H_q][D]
  * bf16; out [num_rows][H_q][D] float32.  Matrix-core kernel (bf16 Q.K^T,
- * fp16 P.V, fp32 accumulation).  Group size <= 8, head_dim 128.
+ * fp16 P.V, fp32 accumulation; V must lie in the fp16 range).  Group size
+ * <= 8, head_dim 128, idx_stride <= 1024.
  * Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
  */
 int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num_rows, const bsa_kv *kv,

@@ -166,6 +166,7 @@ def test_tile_prefill_argument_checks():
     assert call(kvt, tile=32) == _abi.BSA_ERR_UNSUPPORTED
     assert call(kvt, hq=18) == _abi.BSA_ERR_UNSUPPORTED
     assert call(kvt, stride=0) == _abi.BSA_ERR_INVALID_ARG
+    assert call(kvt, stride=1025) == _abi.BSA_ERR_UNSUPPORTED
     assert call(_kv(page_size=64, stride_page=64 * 2 * 128, stride_head=128, stride_token=256, block_table=None,
                     dtype=_abi.BSA_F32, head_dim=128)) == _abi.BSA_ERR_UNSUPPORTED
 
