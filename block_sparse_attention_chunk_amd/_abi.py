@@ -41,6 +41,7 @@ _KV, _CH, _MT, _BG = (ctypes.POINTER(t) for t in (bsa_kv, bsa_chunks, bsa_meta, 
 
 SIGNATURES = {
     "bsa_build_chunk_meta": (ctypes.c_int, [_KV, _CH, _MT, _u32, _P]),
+    "bsa_update_chunk_meta": (ctypes.c_int, [_KV, _CH, _MT, _u32, _P, _i32, _P]),
     "bsa_score_chunks": (ctypes.c_int, [_P, _i32, _i32, _i32, _KV, _CH, _MT, _i32, _i32, _P, _P]),
     "bsa_select_topk": (ctypes.c_int, [_P, _KV, _CH, _BG, _P, _P, _i32, _P]),
     "bsa_router_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),

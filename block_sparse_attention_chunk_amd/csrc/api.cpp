@@ -157,20 +157,40 @@ const char *bsa_status_string(int32_t status) {
 
 const char *bsa_last_error(void) { return g_err; }
 
-int bsa_build_chunk_meta(const bsa_kv *kv, const bsa_chunks *chunks, const bsa_meta *meta, uint32_t which,
-                         void *stream) {
-    bsa::KvView v;
-    bsa::ChunkView c;
-    int rc = check_kv(kv, false, &v);
+static int check_meta_args(const bsa_kv *kv, const bsa_chunks *chunks, const bsa_meta *meta, uint32_t which,
+                           bsa::KvView *v, bsa::ChunkView *c) {
+    int rc = check_kv(kv, false, v);
     if (rc) return rc;
-    if ((rc = check_chunks(kv, chunks, &c))) return rc;
+    if ((rc = check_chunks(kv, chunks, c))) return rc;
     if (!meta) return fail(BSA_ERR_INVALID_ARG, "meta is NULL");
     if (which == 0 || (which & ~(BSA_META_ENVELOPE | BSA_META_CENTROID)))
         return fail(BSA_ERR_INVALID_ARG, "which must be a non-empty combination of BSA_META_* bits");
     if ((which & BSA_META_ENVELOPE) && (!meta->kmin || !meta->kmax))
         return fail(BSA_ERR_INVALID_ARG, "meta->kmin / kmax is NULL");
     if ((which & BSA_META_CENTROID) && !meta->centroid) return fail(BSA_ERR_INVALID_ARG, "meta->centroid is NULL");
-    return launched(bsa::launch_chunk_meta(v, c, meta->kmin, meta->kmax, meta->centroid, which, (hipStream_t)stream));
+    return BSA_OK;
+}
+
+int bsa_build_chunk_meta(const bsa_kv *kv, const bsa_chunks *chunks, const bsa_meta *meta, uint32_t which,
+                         void *stream) {
+    bsa::KvView v;
+    bsa::ChunkView c;
+    int rc = check_meta_args(kv, chunks, meta, which, &v, &c);
+    if (rc) return rc;
+    return launched(bsa::launch_chunk_meta(v, c, meta->kmin, meta->kmax, meta->centroid, which, nullptr, 0,
+                                           (hipStream_t)stream));
+}
+
+int bsa_update_chunk_meta(const bsa_kv *kv, const bsa_chunks *chunks, const bsa_meta *meta, uint32_t which,
+                          const int32_t *from_len, int32_t max_touched, void *stream) {
+    bsa::KvView v;
+    bsa::ChunkView c;
+    int rc = check_meta_args(kv, chunks, meta, which, &v, &c);
+    if (rc) return rc;
+    if (max_touched < 1 || max_touched > c.max_chunks)
+        return fail(BSA_ERR_INVALID_ARG, "max_touched %d must be in [1, max_chunks %d]", max_touched, c.max_chunks);
+    return launched(bsa::launch_chunk_meta(v, c, meta->kmin, meta->kmax, meta->centroid, which, from_len,
+                                           max_touched, (hipStream_t)stream));
 }
 
 int bsa_score_chunks(const void *q, int32_t num_q_heads, int32_t num_rows, int32_t rows_per_query, const bsa_kv *kv,

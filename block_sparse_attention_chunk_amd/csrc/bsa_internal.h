@@ -41,6 +41,17 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // ---- wave-level helpers (wave64) --------------------------------------------
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
+// Max over lanes l, l^16, l^32, l^48 (the same position in the wave's four
+// 16-lane rows) with the gfx950 row-swap instructions: permlane16_swap of a
+// register with itself yields (v[l], v[l^16]) and permlane32_swap yields
+// (v[l], v[l^32]) in every lane; no LDS round trip.
+__device__ __forceinline__ float max_across_rows16(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -89,7 +100,7 @@ struct ChunkView {
 };
 
 hipError_t launch_chunk_meta(const KvView &kv, const ChunkView &ch, void *kmin, void *kmax, float *cen,
-                             uint32_t which, hipStream_t s);
+                             uint32_t which, const int32_t *from_len, int32_t max_touched, hipStream_t s);
 hipError_t launch_score_decode(const void *q, int32_t hq, const KvView &kv, const ChunkView &ch, const void *kmin,
                                const void *kmax, const float *cen, int32_t kind, float *scores, hipStream_t s);
 hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t tile_rows, const KvView &kv,

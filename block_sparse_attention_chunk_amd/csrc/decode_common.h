@@ -110,8 +110,7 @@ __device__ __forceinline__ float softmax_step(const f32x4 &s, int valid, float s
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (4 * G + i < valid) ? s[i] * scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
+    mx = max_across_rows16(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);

@@ -10,29 +10,53 @@
 // chunk's tokens in order (the page of each token comes from the block table,
 // so variable chunks may cross pages).  min / max are exact, the centroid is a
 // float32 sum in token order divided by the token count.  HBM-bound: one read
-// of K, 1/8 (bf16 envelope) of it written back.
+// of K, 1/8 (bf16 envelope) of it written back.  The same kernel refreshes
+// only the chunks that newly appended tokens touched (update mode), with
+// results identical to a full rebuild of those chunks.
 #include "bsa_internal.h"
 
 namespace bsa {
 
+// Update mode (max_touched > 0): wave i of a sequence handles the i-th chunk
+// from the one holding token from_len[b] (the last chunk when from_len is
+// NULL); nothing happens for a sequence with from_len[b] >= its length.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_meta_kernel(KvView kv, ChunkView ch, T *__restrict__ kmin,
                                                          T *__restrict__ kmax, float *__restrict__ cen,
-                                                         uint32_t which) {
+                                                         uint32_t which, const int32_t *__restrict__ from_len,
+                                                         int max_touched) {
     constexpr int VPL = D / 64;  // dims per lane
     const int lane = threadIdx.x & 63;
-    const int c = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    int c = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     const int h = blockIdx.y, b = blockIdx.z;
     const int L = kv.seq_lens[b];
-    int s, e, n;
-    if (ch.starts) {
-        n = ch.num[b];
-        if (c >= n) return;
-        s = ch.starts[(int64_t)b * (ch.max_chunks + 1) + c];
-        e = ch.starts[(int64_t)b * (ch.max_chunks + 1) + c + 1];
+    const int32_t *st = ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr;
+    const int n = st ? ch.num[b] : (L + kv.page - 1) >> kv.log2page;
+    if (max_touched > 0) {
+        if (c >= max_touched) return;
+        int c0 = n - 1;
+        if (from_len) {
+            const int f = from_len[b];
+            if (f >= L) return;
+            if (st) {  // last chunk starting at or before token f
+                int lo = 0, hi = n - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (st[mid] <= f) lo = mid; else hi = mid - 1;
+                }
+                c0 = lo;
+            } else {
+                c0 = f >> kv.log2page;
+            }
+        }
+        c += c0;
+    }
+    if (c >= n) return;
+    int s, e;
+    if (st) {
+        s = st[c];
+        e = st[c + 1];
     } else {
-        n = (L + kv.page - 1) >> kv.log2page;
-        if (c >= n) return;
         s = c << kv.log2page;
         e = min(s + kv.page, L);
     }
@@ -89,23 +113,24 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(KvView kv, ChunkView ch
 }
 
 hipError_t launch_chunk_meta(const KvView &kv, const ChunkView &ch, void *kmin, void *kmax, float *cen,
-                             uint32_t which, hipStream_t s) {
-    dim3 grid((ch.max_chunks + 3) / 4, kv.hkv, kv.batch), block(256);
+                             uint32_t which, const int32_t *from_len, int32_t max_touched, hipStream_t s) {
+    const int span = max_touched > 0 ? max_touched : ch.max_chunks;
+    dim3 grid((span + 3) / 4, kv.hkv, kv.batch), block(256);
+#define BSA_META(T, D)                                                                                       \
+    hipLaunchKernelGGL((chunk_meta_kernel<T, D>), grid, block, 0, s, kv, ch, (T *)kmin, (T *)kmax, cen, which, \
+                       from_len, max_touched)
     if (kv.dtype == BSA_BF16) {
         if (kv.d == 128)
-            hipLaunchKernelGGL((chunk_meta_kernel<uint16_t, 128>), grid, block, 0, s, kv, ch, (uint16_t *)kmin,
-                               (uint16_t *)kmax, cen, which);
+            BSA_META(uint16_t, 128);
         else
-            hipLaunchKernelGGL((chunk_meta_kernel<uint16_t, 64>), grid, block, 0, s, kv, ch, (uint16_t *)kmin,
-                               (uint16_t *)kmax, cen, which);
+            BSA_META(uint16_t, 64);
     } else {
         if (kv.d == 128)
-            hipLaunchKernelGGL((chunk_meta_kernel<float, 128>), grid, block, 0, s, kv, ch, (float *)kmin,
-                               (float *)kmax, cen, which);
+            BSA_META(float, 128);
         else
-            hipLaunchKernelGGL((chunk_meta_kernel<float, 64>), grid, block, 0, s, kv, ch, (float *)kmin,
-                               (float *)kmax, cen, which);
+            BSA_META(float, 64);
     }
+#undef BSA_META
     return hipGetLastError();
 }
 

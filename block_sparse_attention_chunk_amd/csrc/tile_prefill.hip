@@ -265,8 +265,7 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][rt][i]);
-            mx = wave_max_xor(mx, 16);
-            mx = wave_max_xor(mx, 32);
+            mx = max_across_rows16(mx);
             // Lazy rescale: the reference max moves only when a row's max
             // exceeds it by more than 2^8 (weights stay <= 256, well inside
             // fp16), so most blocks skip rescaling the accumulators; the sums

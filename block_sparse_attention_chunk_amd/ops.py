@@ -185,6 +185,18 @@ def build_chunk_meta(kv: KVCache, chunks: Optional[Chunks] = None, which: int = 
     return meta
 
 
+def update_chunk_meta(kv: KVCache, meta: Meta, which: int = BSA_META_ENVELOPE | BSA_META_CENTROID,
+                      from_len: Optional[torch.Tensor] = None, max_touched: int = 1,
+                      chunks: Optional[Chunks] = None) -> Meta:
+    """bsa_update_chunk_meta: refresh the chunks touched by tokens at positions
+    >= from_len[b] (the last chunk when from_len is None) in place."""
+    L = _abi.lib()
+    rc = L.bsa_update_chunk_meta(ctypes.byref(kv.struct()), _chunks_struct(chunks), ctypes.byref(meta.struct()), which,
+                                 _ptr(from_len), int(max_touched), _stream(kv.k.device))
+    _abi.check(rc, "bsa_update_chunk_meta")
+    return meta
+
+
 def score_chunks(q: torch.Tensor, kv: KVCache, meta: Meta, kind: int, rows_per_query: int = 1, causal: bool = False,
                  chunks: Optional[Chunks] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bsa_score_chunks.  Decode: q [B][H_q][D] -> [B][H_kv][max_chunks].

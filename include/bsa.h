@@ -135,6 +135,23 @@ int bsa_build_chunk_meta(const bsa_kv *kv, const bsa_chunks *chunks /* nullable 
                          uint32_t which, void *stream);
 
 /*
+ * Step 1 after tokens were appended (the decode loop): recomputes, per
+ * (sequence, KV head), the chunks whose tokens include positions
+ * >= from_len[b] -- the chunk holding token from_len[b] and the following
+ * ones, at most max_touched of them -- with the rules and results of
+ * bsa_build_chunk_meta (bit-identical to a full rebuild of those chunks).
+ * from_len == NULL refreshes only each sequence's last chunk (one token
+ * appended since the previous call); a sequence with from_len[b] >=
+ * seq_lens[b] is left alone.  kv->seq_lens (and chunks, for variable chunks)
+ * must already describe the grown sequences.  max_touched in
+ * [1, max_chunks]; for fixed pages appending a tokens touches at most
+ * ceil(a / page_size) + 1 chunks.
+ * Errors: as bsa_build_chunk_meta, INVALID_ARG (max_touched).
+ */
+int bsa_update_chunk_meta(const bsa_kv *kv, const bsa_chunks *chunks, const bsa_meta *meta, uint32_t which,
+                          const int32_t *from_len, int32_t max_touched, void *stream);
+
+/*
  * Step 2: chunk scores.  score_kind BSA_ENVELOPE or BSA_CENTROID ([P1]).
  * Scores are raw dot products (no 1/sqrt(d)); for selection per KV head the
  * scores of a GQA group's query heads are combined by their maximum.

@@ -212,3 +212,16 @@ def test_merge_and_partials_argument_checks():
     kv = _kv()
     rc = L.bsa_sparse_attn_decode(FAKE, 8, ctypes.byref(kv), None, FAKE, FAKE, 8, 0.088, 1, None, None, 0, None)
     assert rc == _abi.BSA_ERR_INVALID_ARG and "out may be NULL" in L.bsa_last_error().decode()
+
+
+def test_update_meta_argument_checks():
+    L = _abi.lib()
+    kv = _kv()
+    m = _abi.bsa_meta(FAKE, FAKE, FAKE)
+    def upd(mt, which=3, meta=ctypes.byref(m)):
+        return L.bsa_update_chunk_meta(ctypes.byref(kv), None, meta, which, None, mt, None)
+    assert upd(0) == _abi.BSA_ERR_INVALID_ARG
+    assert upd(65) == _abi.BSA_ERR_INVALID_ARG                # max_pages is 64
+    assert upd(1, which=0) == _abi.BSA_ERR_INVALID_ARG
+    assert upd(1, meta=None) == _abi.BSA_ERR_INVALID_ARG
+    assert "max_touched" in (upd(0) and L.bsa_last_error().decode())

@@ -253,3 +253,13 @@ def test_fused_token_budget_fixed_pages(dev):
                              head_dim=128, name="tokens-fixed")
     run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.token_budget(1000), band_exact_count=False,
                     splits=(0, 3), check_dense=False)
+
+
+@pytest.mark.parametrize("k", [64, 32])
+def test_varchunk_centroid_topk(dev, k):
+    """TSA chunking with centroid scoring and a chunk-count budget (top_k
+    chunks per KV head, the tk64 / tk32 variants)."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.varchunk_decode()
+    r = run_decode_case(case, dev, ops.BSA_CENTROID, ops.Budget.topk(k), check_dense=False, splits=(0, 5))
+    assert np.all(r["cnt"] == k)
