@@ -105,14 +105,21 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
             m[i] = base + i < n && (keys[i] & pmask) == prefix;
             dg[i] = (keys[i] >> shift) & 255u;
         }
-        int acc = 0;
+        // after the first passes few candidates still match: a wave with none
+        // skips the block
+        bool any = false;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            acc += m[i] ? wts[i] : 0;
-            bool last = m[i];
-            if (i + 1 < PER) last = last && !(m[i + 1] && dg[i + 1] == dg[i]);
-            if (last) atomicAdd(&H[sub][dg[i]], acc);
-            acc = last ? 0 : acc;
+        for (int i = 0; i < PER; ++i) any = any || m[i];
+        if (__ballot(any)) {
+            int acc = 0;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                acc += m[i] ? wts[i] : 0;
+                bool last = m[i];
+                if (i + 1 < PER) last = last && !(m[i + 1] && dg[i + 1] == dg[i]);
+                if (last) atomicAdd(&H[sub][dg[i]], acc);
+                acc = last ? 0 : acc;
+            }
         }
         __syncthreads();
         // every wave: lane l holds digits 255-4l .. 252-4l (descending)
