@@ -24,8 +24,10 @@ replayed, so host dispatch is not in the measurement.
 Extra records in the same JSON line: the same layer with 16 sequences at
 32,768 tokens; a 64 q / 8 KV-head batch of 16 x 32,768 tokens at ratio 1/8
 (4096 tokens per sequence and head); the 131,072-token router prefill (28 q /
-4 KV heads, k = 32, rho = 2) with its MFMA utilisation; with --extra also the
-seven ratios of the 8K-32K batched workload, both scorings.
+4 KV heads, k = 32, rho = 2) with its MFMA utilisation, and the same router
+at 32,768 and 65,536 tokens; a 48-layer decode step (48 replay-shaped layers
+with their own caches, one HIP graph) at 1 and 16 sequences; with --extra
+also the seven ratios of the 8K-32K batched workload, both scorings.
 
 Prints one JSON line.  --gpus N > 1 is refused (one GPU per box).
 """
@@ -59,7 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-batched", action="store_true", help="skip the batched extra records")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the router prefill record")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the router prefill records")
+    ap.add_argument("--no-layers", action="store_true", help="skip the 48-layer decode-step records")
     ap.add_argument("--extra", action="store_true", help="also the seven-ratio batched sweep")
     ap.add_argument("--only-headline-kernel", action="store_true",
                     help="profiling aid: time only the headline workload")
@@ -384,6 +387,74 @@ class PrefillBench:
         }
 
 
+class LayerStackBench:
+    """A serving-shaped decode step: `layers` replay-shaped layers, each with
+    its own K/V cache and metadata (device copies of one generated layer),
+    every layer running scoring + fused selection / attention + merge; the
+    whole step is one HIP graph."""
+
+    def __init__(self, case, budget, scoring, dev, layers=48):
+        import torch
+        from block_sparse_attention_chunk_amd import ops
+        self.ops, self.torch, self.case, self.dev, self.layers = ops, torch, case, dev, layers
+        self.kind = ops.BSA_ENVELOPE if scoring == "envelope" else ops.BSA_CENTROID
+        which = ops.BSA_META_ENVELOPE if self.kind == ops.BSA_ENVELOPE else ops.BSA_META_CENTROID
+        self.budget = budget
+        k0, v0 = ops.upload(case.k, dev), ops.upload(case.v, dev)
+        bt, sl = ops.upload(case.block_table, dev), ops.upload(case.seq_lens, dev)
+        self.q = ops.upload(case.q, dev)
+        self.stack = []
+        for i in range(layers):
+            kv = ops.KVCache(k0 if i == 0 else k0.clone(), v0 if i == 0 else v0.clone(), sl, case.page_size, bt)
+            self.stack.append((kv, ops.build_chunk_meta(kv, which=which)))
+        kv0 = self.stack[0][0]
+        B, H = case.batch, case.num_kv_heads
+        self.scores = torch.empty((B, H, kv0.max_pages), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
+        K = budget.max_selected(kv0.max_pages)
+        self.ws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, K), 1),), dtype=torch.uint8,
+                              device=dev)
+        self.dws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, kv0.max_pages), 1),),
+                               dtype=torch.uint8, device=dev)
+
+    def step(self):
+        ops = self.ops
+        for kv, meta in self.stack:
+            ops.score_chunks(self.q, kv, meta, self.kind, out=self.scores)
+            ops.select_attn_decode(self.q, kv, self.scores, self.budget, out=self.out, workspace=self.ws)
+
+    def dense_step(self):
+        for kv, _ in self.stack:
+            self.ops.sparse_attn_decode(self.q, kv, None, None, out=self.out, workspace=self.dws)
+
+    def measure(self, steps=20):
+        torch = self.torch
+        res = {}
+        for name, fn in (("sparse", self.step), ("dense", self.dense_step)):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            g.replay()
+            torch.cuda.synchronize()
+            n = steps if name == "sparse" else max(2, steps // 4)
+            t0 = time.perf_counter()
+            for _ in range(n):
+                g.replay()
+            torch.cuda.synchronize()
+            res[name] = (time.perf_counter() - t0) / n
+            del g
+        case = self.case
+        return {"workload": f"{self.layers}-layer decode step, replay-shaped layers (32 q / 4 KV heads, d 128, "
+                            f"bf16), {case.batch} x {int(case.seq_lens.max())} tokens, top-256 pages per KV head",
+                "layers": self.layers, "batch": case.batch,
+                "tokens_per_s": case.batch / res["sparse"], "ms_per_token_step": res["sparse"] * 1e3,
+                "us_per_layer": res["sparse"] / self.layers * 1e6,
+                "dense_ms_per_token_step": res["dense"] * 1e3,
+                "speedup_vs_dense_attention": res["dense"] / res["sparse"]}
+
+
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_decode_replay_b1_hbm_traffic.txt")
 KERNEL_SOURCES = ["select_decode.hip", "decode_common.h", "radix_select.h", "select_rules.h"]
 
@@ -509,6 +580,28 @@ def main():
         res["prefill"] = pb.measure()
         del pb, pc
         torch.cuda.empty_cache()
+        by_len = []
+        for T in (32768, 65536):
+            log(f"router prefill: {T} tokens")
+            pc = synth.router_prefill(T=T, groups=max(4, T // 8192), tied_groups=tuple(range(3, max(4, T // 8192), 4)))
+            pb = PrefillBench(pc, dev, ops.BSA_ENVELOPE)
+            m = pb.measure()
+            by_len.append({k: m[k] for k in ("workload", "tokens_per_s", "sparse_pipeline_ms", "tile_score_ms",
+                                             "router_ms", "sparse_attn_ms", "dense_causal_attn_ms",
+                                             "sparse_pipeline_vs_dense_attn", "triggered_tiles", "attn_mfma_frac")})
+            del pb, pc
+            torch.cuda.empty_cache()
+        res["prefill_by_length"] = by_len
+    if not a.no_layers and not a.only_headline_kernel:
+        stacks = []
+        for B, L in ((1, None), (16, 32768)):
+            log(f"48-layer decode step, {B} sequence(s)")
+            c = synth.replay_decode() if L is None else synth.replay_decode(seq_len=L, batch=B)
+            lb = LayerStackBench(c, ops.Budget.topk(256), "envelope", dev)
+            stacks.append(lb.measure())
+            del lb, c
+            torch.cuda.empty_cache()
+        res["layer_stack"] = stacks
     if a.extra:
         log("ratio sweep: 16 sequences of 8K-32K tokens, 64 q / 8 KV heads")
         c3 = synth.batched_decode()
