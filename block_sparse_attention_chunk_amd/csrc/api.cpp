@@ -293,6 +293,13 @@ size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t
     return (size_t)kv->batch * num_q_heads * s * (kv->head_dim + 2) * sizeof(float);
 }
 
+// Decode outputs and split partials are written as 16-byte vectors.
+static int check_out_ws(const float *out, const void *workspace) {
+    if (out && !aligned16(out)) return fail(BSA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if (workspace && !aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return BSA_OK;
+}
+
 int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_chunks *chunks,
                            const int32_t *sel_idx, const int32_t *sel_count, int32_t max_sel, float softmax_scale,
                            int32_t num_splits, float *out, void *workspace, size_t workspace_bytes, void *stream) {
@@ -317,6 +324,7 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
     const size_t need = bsa_decode_workspace_bytes(kv, num_q_heads, items, splits);
     if (need && (!workspace || workspace_bytes < need))
         return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if ((rc = check_out_ws(out, need ? workspace : nullptr))) return rc;
     return launched(bsa::launch_decode(q, num_q_heads, v, c, sel_idx, sel_count, max_sel, softmax_scale, splits, out,
                                        workspace, (hipStream_t)stream));
 }
@@ -354,6 +362,7 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
     const size_t ws_need = bsa_decode_workspace_bytes(kv, num_q_heads, (int)need, splits);
     if (ws_need && (!workspace || workspace_bytes < ws_need))
         return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", ws_need, workspace_bytes);
+    if ((rc = check_out_ws(out, ws_need ? workspace : nullptr))) return rc;
     return launched(bsa::launch_select_decode(q, num_q_heads, v, scores, *budget, sel_idx, sel_count,
                                               sel_idx ? max_sel : 0, softmax_scale, splits, out, workspace,
                                               (hipStream_t)stream));
@@ -365,6 +374,7 @@ int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, 
     if (batch < 1 || num_q_heads < 1) return fail(BSA_ERR_INVALID_ARG, "batch and num_q_heads must be >= 1");
     if (head_dim != 64 && head_dim != 128) return fail(BSA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", head_dim);
     if (num_splits < 2 || num_splits > 64) return fail(BSA_ERR_INVALID_ARG, "num_splits must be in [2, 64]");
+    if (int rc = check_out_ws(out, workspace)) return rc;
     const float *part_o = (const float *)workspace;
     const float *part_ml = part_o + (size_t)batch * num_q_heads * num_splits * head_dim;
     return launched(bsa::launch_decode_merge(num_splits, part_o, part_ml, out, num_q_heads, batch, head_dim,

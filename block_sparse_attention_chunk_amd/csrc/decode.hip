@@ -159,14 +159,14 @@ __global__ __launch_bounds__(256) void decode_chunked_kernel(const T *__restrict
 // Merge of the splits of one (sequence, query head):
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
 // One wave per row; lane s holds split s's (m, l) (splits <= 64) and every
-// lane owns D/64 output dims.  All loads of a batch of 16 splits are issued
+// lane owns D/64 output dims.  All loads of a batch of 32 splits are issued
 // before the first use (clamped to the last split), so the kernel waits on
 // memory once per batch.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(int splits, const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, float *__restrict__ out,
                                                           int hq) {
-    constexpr int VD = D / 64, SB = 16;
+    constexpr int VD = D / 64, SB = 32;
     const int j = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int64_t row = (int64_t)b * hq + j;
     const float2 ml = reinterpret_cast<const float2 *>(part_ml + row * splits * 2)[min(lane, splits - 1)];

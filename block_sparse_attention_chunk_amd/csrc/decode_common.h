@@ -286,28 +286,34 @@ __device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float 
             for (int dd = 0; dd < VD; ++dd) ob[j * D + VD * lane + dd] = st.acc[j][dd];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < g * D; idx += kDecWaves * 64) {
-        const int j = idx / D, d = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, mbuf[ww * 16 + j]);
-        float o = 0.f, l = 0.f;
+    // each thread merges 4 consecutive dims of one head
+    constexpr int D4 = D / 4;
+    for (int idx = threadIdx.x; idx < g * D4; idx += kDecWaves * 64) {
+        const int j = idx / D4, d = (idx % D4) * 4;
+        float mw[kDecWaves], M = -INFINITY;
 #pragma unroll
         for (int ww = 0; ww < kDecWaves; ++ww) {
-            const float mw = mbuf[ww * 16 + j];
-            const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-            o = fmaf(f, regions[ww * R + j * D + d], o);
+            mw[ww] = mbuf[ww * 16 + j];
+            M = fmaxf(M, mw[ww]);
+        }
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float l = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kDecWaves; ++ww) {
+            const float f = mw[ww] == -INFINITY ? 0.f : exp2f(mw[ww] - M);
+            const float4 r = *reinterpret_cast<const float4 *>(regions + ww * R + j * D + d);
+            o.x = fmaf(f, r.x, o.x);
+            o.y = fmaf(f, r.y, o.y);
+            o.z = fmaf(f, r.z, o.z);
+            o.w = fmaf(f, r.w, o.w);
             l = fmaf(f, lbuf[ww * 16 + j], l);
         }
         const int64_t row = (int64_t)b * hq + h * g + j;
         if (splits == 1) {
-            out[row * D + d] = o / l;
+            *reinterpret_cast<float4 *>(out + row * D + d) = make_float4(o.x / l, o.y / l, o.z / l, o.w / l);
         } else {
-            part_o[(row * splits + split) * D + d] = o;
-            if (d == 0) {
-                part_ml[(row * splits + split) * 2] = M;
-                part_ml[(row * splits + split) * 2 + 1] = l;
-            }
+            *reinterpret_cast<float4 *>(part_o + (row * splits + split) * D + d) = o;
+            if (d == 0) *reinterpret_cast<float2 *>(part_ml + (row * splits + split) * 2) = make_float2(M, l);
         }
     }
 }

@@ -73,12 +73,16 @@ __device__ __forceinline__ void block_scan_pair(int &a, int &b, RadixShared &sh,
 }
 
 // keys[PER] / wts[PER] (weights >= 1): this thread's candidates (index
-// base + i, valid when base + i < n <= 65535).  Returns the number kept;
-// emit(pos, index, i) is called once for every kept candidate, pos being its
-// rank in ascending index order and i its slot in this thread's arrays.  The total weight must stay below 2^31.
-template <int NT, int PER, typename Emit>
+// base + i, valid when base + i < n <= 65535).  Returns the number kept.
+// emit(keep, pos, index, i) is called once for every slot i of this thread,
+// in order; for a kept candidate, pos is its rank in ascending index order.  A
+// thread's kept candidates take consecutive ranks: begin(p) is called once per
+// thread, before its first emit, with the rank its first kept candidate gets
+// (or would get).  The total weight must stay below 2^31.
+template <int NT, int PER, typename Begin, typename Emit>
 __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[PER], const int (&wts)[PER], int base,
-                                                        int n, int64_t budget, Emit emit, RadixShared &sh) {
+                                                        int n, int64_t budget, Begin begin, Emit emit,
+                                                        RadixShared &sh) {
     const int tid = threadIdx.x, lane = tid & 63, sub = (tid >> 6) & 1;
     const int bud = (int)min(budget, (int64_t)0x7fffffff);
     int *flat0 = &sh.hist[0][0][0];
@@ -162,15 +166,16 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
 
     // one scan of (count > T | count == T << 16, weight == T): ranks of the
     // kept candidates in index order
+    bool gt[PER], eq[PER];
     int gtc = 0, eqc = 0, eqw = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        if (base + i < n) {
-            const bool gt = all || keys[i] > T, eq = !all && keys[i] == T;
-            gtc += gt ? 1 : 0;
-            eqc += eq ? 1 : 0;
-            eqw += eq ? wts[i] : 0;
-        }
+        const bool v = base + i < n;
+        gt[i] = v && (all || keys[i] > T);
+        eq[i] = v && !all && keys[i] == T;
+        gtc += gt[i] ? 1 : 0;
+        eqc += eq[i] ? 1 : 0;
+        eqw += eq[i] ? wts[i] : 0;
     }
     int a = gtc | (eqc << 16), b = eqw, ta, tb;
     block_scan_pair<NT>(a, b, sh, ta, tb);
@@ -178,28 +183,27 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
     b -= eqw;
     int gt_before = a & 0xffff, eq_before = a >> 16;
     // the first candidate == T that no longer fits: its tie rank is the number
-    // of ties kept (none such: every tie is kept)
-    if (!all) {
+    // of ties kept (none such: every tie is kept).  At most one thread finds it.
+    int hit = -1;
+    {
         int ce = eq_before, r = b;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            if (base + i < n && keys[i] == T) {
-                if (r <= remaining && r + wts[i] > remaining) sh.esel = ce;
-                r += wts[i];
-                ++ce;
-            }
+            hit = (eq[i] && r <= remaining && r + wts[i] > remaining) ? ce : hit;
+            r += eq[i] ? wts[i] : 0;
+            ce += eq[i] ? 1 : 0;
         }
     }
+    if (hit >= 0) sh.esel = hit;
     __syncthreads();
     const int e_sel = sh.esel < 0 ? (ta >> 16) : sh.esel;
+    begin(gt_before + min(eq_before, e_sel));
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        if (base + i < n) {
-            const bool gt = all || keys[i] > T, eq = !all && keys[i] == T;
-            if (gt || (eq && eq_before < e_sel)) emit(gt_before + min(eq_before, e_sel), base + i, i);
-            gt_before += gt ? 1 : 0;
-            eq_before += eq ? 1 : 0;
-        }
+        const bool keep = gt[i] || (eq[i] && eq_before < e_sel);
+        emit(keep, gt_before + min(eq_before, e_sel), base + i, i);
+        gt_before += gt[i] ? 1 : 0;
+        eq_before += eq[i] ? 1 : 0;
     }
     (void)tb;
     return (ta & 0xffff) + e_sel;
@@ -210,9 +214,10 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
 template <int NT, int PER>
 __device__ __forceinline__ int radix_select_prefix(const uint32_t (&keys)[PER], const int (&wts)[PER], int base,
                                                    int n, int64_t budget, int *dst, int dst_cap, RadixShared &sh) {
-    const int total = radix_select_prefix_emit<NT, PER>(keys, wts, base, n, budget, [&](int pos, int idx, int) {
-        if (pos < dst_cap) dst[pos] = idx;
-    }, sh);
+    const int total = radix_select_prefix_emit<NT, PER>(
+        keys, wts, base, n, budget, [](int) {}, [&](bool keep, int pos, int idx, int) {
+            if (keep && pos < dst_cap) dst[pos] = idx;
+        }, sh);
     return min(total, dst_cap);
 }
 

@@ -52,12 +52,16 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
     for (int i = 0; i < PER; ++i) raw[i] = row[min(base + i, mc - 1)];
     // the block-table entries of the same candidates, so the kept pages come
     // with their physical numbers and the attention needs no lookup
-    const int32_t *bt = kv.bt ? kv.bt + (int64_t)b * kv.max_pages : nullptr;
+    // (without a block table the load reads the score row instead, so it stays
+    // unconditional and the memory waits stay exact)
+    const bool has_bt = kv.bt != nullptr;
+    const int32_t *btr = has_bt ? kv.bt + (int64_t)b * kv.max_pages : reinterpret_cast<const int32_t *>(row);
     int phys[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int c = min(base + i, mc - 1);
-        phys[i] = bt ? bt[c] : b * kv.max_pages + c;
+        const int v = btr[c];
+        phys[i] = has_bt ? v : b * kv.max_pages + c;
     }
     uint4 qb[NW];
     load_q_operand<T, D>(q, hq, g, b, h, lane, qb);
@@ -69,13 +73,28 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
     int wts[PER];
     select_keys<PER>(raw, base, n, rb, nullptr, L, 16, 4, keys, wts);
     int32_t *dst = (split == 0 && sel_idx) ? sel_idx + ((int64_t)b * kv.hkv + h) * max_sel : nullptr;
-    const int cnt = radix_select_prefix_emit<256, PER>(keys, wts, base, n, rb.budget, [&](int pos, int idx, int i) {
-        if (dst && pos < max_sel) dst[pos] = idx;
-        if (pos % splits == split) {  // pos / splits < kFusedListCap (host-checked)
-            list[pos / splits] = idx;
-            plist[pos / splits] = phys[i];
-        }
-    }, sh);
+    // rank p goes to split p mod splits, slot p / splits; a thread's kept pages
+    // have consecutive ranks, so one division per thread sets (slot, split)
+    // and each kept page steps it
+    int qs = 0, rs = 0;
+    const int cnt = radix_select_prefix_emit<256, PER>(
+        keys, wts, base, n, rb.budget,
+        [&](int p0) {
+            qs = p0 / splits;
+            rs = p0 - qs * splits;
+        },
+        [&](bool keep, int pos, int idx, int i) {
+            if (dst && keep && pos < max_sel) dst[pos] = idx;
+            if (keep && rs == split) {  // qs < kFusedListCap (host-checked)
+                list[qs] = idx;
+                plist[qs] = phys[i];
+            }
+            rs += keep ? 1 : 0;
+            const bool wrap = rs == splits;
+            rs = wrap ? 0 : rs;
+            qs += wrap ? 1 : 0;
+        },
+        sh);
     if (dst) {
         for (int i = cnt + (int)threadIdx.x; i < max_sel; i += 256) dst[i] = -1;
         if (threadIdx.x == 0) sel_count[(int64_t)b * kv.hkv + h] = min(cnt, max_sel);

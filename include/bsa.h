@@ -227,7 +227,8 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * runs an online softmax for the whole GQA group and the parts are merged.
  * sel_idx [batch][H_kv][max_sel] / sel_count [batch][H_kv] as produced by
  * bsa_select_topk; sel_idx == NULL attends to every chunk (dense baseline).
- * q [batch][H_q][D] (kv dtype); out [batch][H_q][D] float32.
+ * q [batch][H_q][D] (kv dtype); out [batch][H_q][D] float32; q, out and
+ * workspace 16-byte aligned.
  * Group size H_q/H_kv <= 16.  workspace >= bsa_decode_workspace_bytes(...)
  * (0 bytes when the resolved split count is 1): the split partials, merged
  * by a second kernel on the same stream.  Splits are capped at 64.  Calls that
@@ -249,7 +250,8 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
  * per-split outputs) followed by (m, l) [batch][H_q][num_splits][2] float32
  * (per-split running max of the base-2 scaled logits and softmax sum);
  *   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
- * num_splits in [2, 64]; head_dim 64 or 128.  out [batch][H_q][head_dim].
+ * num_splits in [2, 64]; head_dim 64 or 128.  out [batch][H_q][head_dim];
+ * out and workspace 16-byte aligned.
  * Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
  */
 int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, int32_t head_dim,
@@ -270,7 +272,7 @@ int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, 
  * pages; workspace >= bsa_decode_workspace_bytes(kv, H_q, K, num_splits).
  * max_pages <= 8192; group size <= 16.  Calls sharing a workspace must not
  * overlap.  out may be NULL with more than one split, as for
- * bsa_sparse_attn_decode.
+ * bsa_sparse_attn_decode; q, out and workspace 16-byte aligned.
  * Errors: INVALID_ARG, UNSUPPORTED (page size, limits), WORKSPACE, LAUNCH.
  */
 int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,

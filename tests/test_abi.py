@@ -225,3 +225,25 @@ def test_update_meta_argument_checks():
     assert upd(1, which=0) == _abi.BSA_ERR_INVALID_ARG
     assert upd(1, meta=None) == _abi.BSA_ERR_INVALID_ARG
     assert "max_touched" in (upd(0) and L.bsa_last_error().decode())
+
+
+def test_decode_outputs_must_be_16_byte_aligned():
+    L = _abi.lib()
+    kv = _kv()
+    need = L.bsa_decode_workspace_bytes(ctypes.byref(kv), 8, 8, 4)
+    # unfused decode: out, then workspace
+    rc = L.bsa_sparse_attn_decode(FAKE, 8, ctypes.byref(kv), None, FAKE, FAKE, 8, 0.088, 1, FAKE + 8, None, 0, None)
+    assert rc == _abi.BSA_ERR_INVALID_ARG and "out must be 16-byte aligned" in L.bsa_last_error().decode()
+    rc = L.bsa_sparse_attn_decode(FAKE, 8, ctypes.byref(kv), None, FAKE, FAKE, 8, 0.088, 4, FAKE, FAKE + 4, need, None)
+    assert rc == _abi.BSA_ERR_INVALID_ARG and "workspace must be 16-byte aligned" in L.bsa_last_error().decode()
+    # fused selection + decode
+    top = _abi.bsa_budget(_abi.BSA_BUDGET_TOPK, 8, 0, 0, 0, 0.0)
+    rc = L.bsa_select_attn_decode(FAKE, 8, ctypes.byref(kv), FAKE, ctypes.byref(top), 0.088, 4, FAKE + 4,
+                                  None, None, 0, FAKE, need, None)
+    assert rc == _abi.BSA_ERR_INVALID_ARG and "out must be 16-byte aligned" in L.bsa_last_error().decode()
+    rc = L.bsa_select_attn_decode(FAKE, 8, ctypes.byref(kv), FAKE, ctypes.byref(top), 0.088, 4, FAKE,
+                                  None, None, 0, FAKE + 8, need, None)
+    assert rc == _abi.BSA_ERR_INVALID_ARG and "workspace" in L.bsa_last_error().decode()
+    # merge
+    assert L.bsa_decode_merge(FAKE + 4, 1, 8, 128, 4, FAKE, None) == _abi.BSA_ERR_INVALID_ARG
+    assert L.bsa_decode_merge(FAKE, 1, 8, 128, 4, FAKE + 8, None) == _abi.BSA_ERR_INVALID_ARG
