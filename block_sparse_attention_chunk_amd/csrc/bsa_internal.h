@@ -59,6 +59,21 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---- kernel arguments ----------------------------------------------------------
+// Arguments reach the scalar registers by scalar loads that the compiler emits
+// at first use; spread over a kernel's prologue they form a chain of dependent
+// round trips ahead of the first memory requests.  Naming the arguments the
+// first requests need here makes the compiler fetch them together, with a
+// single wait.
+template <typename A>
+__device__ __forceinline__ void arg_ready(const A &a) {
+    asm volatile("" ::"s"(a));
+}
+template <typename... A>
+__device__ __forceinline__ void args_ready(const A &...a) {
+    (arg_ready(a), ...);
+}
+
 // ---- block-wide inclusive scans over 256 threads (4 waves) ------------------
 // Returns the inclusive prefix of v over threadIdx.x; *total gets the block sum.
 // `scratch` needs 8 ints of shared memory.  All 256 threads must call it.

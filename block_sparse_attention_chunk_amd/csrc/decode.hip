@@ -46,6 +46,7 @@ void decode_paged16_kernel(const T *__restrict__ q, int hq, KvView kv, const int
     constexpr int NW = DecTraits<T, D>::kNW, R = region_floats<D, GP>();
     __shared__ __attribute__((aligned(16))) float regions[kDecWaves * R];
     __shared__ float mbuf[kDecWaves * 16], lbuf[kDecWaves * 16];
+    args_ready(q, hq, kv.hkv, kv.bt, kv.seq_lens, kv.max_pages, sel_idx, sel_count, max_sel, splits);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int g = hq / kv.hkv;
@@ -57,13 +58,21 @@ void decode_paged16_kernel(const T *__restrict__ q, int hq, KvView kv, const int
     const int wstride = splits * kDecWaves;
     const int first = split + splits * w;
     int spec = first + wstride * lane;
-    if (items) spec = items[min(spec, max_sel - 1)];
-    const int L = kv.seq_lens[b];
-    const int npages = (L + 15) >> 4;
-    const int nitems = sel_idx ? sel_count[(int64_t)b * kv.hkv + h] : npages;
-
+    // The page numbers, the item count, the row length and the query are
+    // requested together, unconditionally (without a selection the spare
+    // loads read the row length), and waited for once.
+    const int32_t *spec_src = items ? items : kv.seq_lens;
+    int spec_ld = spec_src[items ? min(spec, max_sel - 1) : b];
+    const int32_t *cnt_src = sel_idx ? sel_count + ((int64_t)b * kv.hkv + h) : kv.seq_lens + b;
+    int cnt_ld = *cnt_src;
+    int len_ld = kv.seq_lens[b];
     uint4 qb[NW];
     load_q_operand<T, D>(q, hq, g, b, h, lane, qb);
+    asm volatile("" : "+v"(spec_ld), "+v"(cnt_ld), "+v"(len_ld)::"memory");
+    if (items) spec = spec_ld;
+    const int L = __builtin_amdgcn_readfirstlane(len_ld);
+    const int npages = (L + 15) >> 4;
+    const int nitems = sel_idx ? __builtin_amdgcn_readfirstlane(cnt_ld) : npages;
     WaveState<T, D, GP> st;
     init_state(st);
 
@@ -167,6 +176,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(int splits, const floa
                                                           const float *__restrict__ part_ml, float *__restrict__ out,
                                                           int hq) {
     constexpr int VD = D / 64, SB = 32;
+    args_ready(splits, part_o, part_ml, hq);
     const int j = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int64_t row = (int64_t)b * hq + j;
     const float2 ml = reinterpret_cast<const float2 *>(part_ml + row * splits * 2)[min(lane, splits - 1)];

@@ -322,11 +322,16 @@ template <typename T, int D>
 __device__ __forceinline__ void load_q_operand(const T *__restrict__ q, int hq, int g, int b, int h, int lane,
                                                uint4 (&qb)[DecTraits<T, D>::kNW]) {
     const int n16 = lane & 15, G = lane >> 4;
-    if (n16 < g) {
-        load_k_slice<T, D>(q + ((int64_t)b * hq + h * g + n16) * D, qb, G);
-    } else {
+    // unconditional (padding columns read a real head and are masked), so the
+    // load never sits in a branch that would force a full memory wait
+    load_k_slice<T, D>(q + ((int64_t)b * hq + h * g + min(n16, g - 1)) * D, qb, G);
+    const uint32_t m = n16 < g ? 0xffffffffu : 0u;
 #pragma unroll
-        for (int i = 0; i < DecTraits<T, D>::kNW; ++i) qb[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < DecTraits<T, D>::kNW; ++i) {
+        qb[i].x &= m;
+        qb[i].y &= m;
+        qb[i].z &= m;
+        qb[i].w &= m;
     }
 }
 

@@ -3,21 +3,24 @@
 //
 // Candidates are ordered by (score descending, index ascending).  With a
 // weight per candidate, the selection is the longest prefix of that order
-// whose total weight fits the budget.  Four 8-bit passes over
+// whose total weight fits the budget.  Up to four 8-bit passes over
 // order-preserving float keys find the key T of the first candidate that does
 // not fit; every key > T is kept, and the candidates with key == T are kept in
 // ascending index order while their running weight still fits.  The kept ids
 // come out in ascending index order from one block scan, so ties need no sort.
 //
 // One workgroup of NT threads per row; each thread holds PER consecutive
-// candidates in registers (n <= NT * PER).  Per pass: histogram atomics into
-// one of three rotating LDS histograms (two sub-histograms, even / odd waves),
-// one barrier, then every wave finds the crossing digit itself (lane l owns
-// digits 255-4l .. 252-4l, a DPP wave scan gives the weight above them), so
-// no second barrier broadcasts it.  A
-// histogram is cleared two passes after it was read, so clearing needs no
-// barrier of its own.  The total weight falls out of the first pass, and the
-// passes stop early when the cut lands on a digit boundary.
+// candidates in registers (n <= NT * PER).  The passes start below the leading
+// bits that the smallest and the largest key share (scores of one row usually
+// share sign and most of the exponent, so a pass over those bits would rank
+// nothing).  Per pass: histogram atomics into one of three rotating LDS
+// histograms (two sub-histograms, even / odd waves), one barrier, then every
+// wave finds the crossing digit itself (lane l owns digits 255-4l .. 252-4l,
+// a DPP wave scan gives the weight above them), so no second barrier
+// broadcasts it.  A histogram is cleared two passes after it was read, so
+// clearing needs no barrier of its own.  The total weight falls out of the
+// first pass, and the passes stop early when the cut lands on a digit
+// boundary.
 #pragma once
 
 #include "bsa_internal.h"
@@ -27,6 +30,7 @@ namespace bsa {
 struct RadixShared {
     int hist[3][2][256];
     int wsum[2][16];    // per-wave partials of the block scan (<= 16 waves)
+    int wext[16];       // per-wave weight of the forced candidates
     int esel;           // number of kept candidates with key == T (-1: all of them)
 };
 
@@ -41,6 +45,18 @@ __device__ __forceinline__ int wave_scan_incl(int x) {
     x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
     x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return x;
+}
+
+// Maximum over the 64 lanes of a wave (same shift pattern as the scan; lanes
+// outside a shift's source range contribute 0).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // Inclusive block scan of two values at once over NT threads; totals in ta /
@@ -83,18 +99,55 @@ template <int NT, int PER, typename Begin, typename Emit>
 __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[PER], const int (&wts)[PER], int base,
                                                         int n, int64_t budget, Begin begin, Emit emit,
                                                         RadixShared &sh) {
-    const int tid = threadIdx.x, lane = tid & 63, sub = (tid >> 6) & 1;
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, sub = wid & 1;
     const int bud = (int)min(budget, (int64_t)0x7fffffff);
+    // Forced candidates (key 0xffffffff, which no finite score has) are kept
+    // outright; the passes rank the others.  Their keys all lie between the
+    // smallest and the largest of them and so share those two keys' leading
+    // bits: the first pass starts below those bits.
+    bool cand[PER];
+    uint32_t tmax = 0, tnmin = 0;
+    int tforced = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const bool v = base + i < n, f = keys[i] == 0xffffffffu;
+        cand[i] = v && !f;
+        tmax = max(tmax, cand[i] ? keys[i] : 0u);
+        tnmin = max(tnmin, cand[i] ? ~keys[i] : 0u);
+        tforced += (v && f) ? wts[i] : 0;
+    }
+    tmax = wave_max_u32(tmax);
+    tnmin = wave_max_u32(tnmin);
+    tforced = __builtin_amdgcn_readlane(wave_scan_incl(tforced), 63);
+    if (lane == 0) {
+        sh.wsum[0][wid] = (int)tmax;
+        sh.wsum[1][wid] = (int)tnmin;
+        sh.wext[wid] = tforced;
+    }
     int *flat0 = &sh.hist[0][0][0];
     for (int i = tid; i < 512; i += NT) flat0[i] = 0;
     if (tid == 0) sh.esel = -1;
     __syncthreads();
+    uint32_t kmax = 0, kmin = 0xffffffffu;
+    int forced = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        kmax = max(kmax, (uint32_t)sh.wsum[0][w]);
+        kmin = min(kmin, ~(uint32_t)sh.wsum[1][w]);
+        forced += sh.wext[w];
+    }
+    // bits above `hi` are common to every ranked candidate (none ranked:
+    // kmin > kmax, and every bit is left to the passes)
+    const int cp = kmin <= kmax ? __clz((int)(kmin ^ kmax)) : 0;
+    const int hi = max(32 - cp, 8);
 
     bool all = false;
-    uint32_t prefix = 0, pmask = 0;
-    int wabove = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
+    uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+    uint32_t prefix = kmax & pmask;
+    int wabove = forced;  // weight ranked above the current bucket
+    for (int pass = 0;; ++pass) {
+        const int shift = max(hi - 8 * (pass + 1), 0);
         int(*H)[256] = sh.hist[pass % 3];
         int *next = &sh.hist[(pass + 1) % 3][0][0];  // last read two passes ago
         for (int i = tid; i < 512; i += NT) next[i] = 0;
@@ -106,7 +159,7 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
         int dg[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            m[i] = base + i < n && (keys[i] & pmask) == prefix;
+            m[i] = cand[i] && (keys[i] & pmask) == prefix;
             dg[i] = (keys[i] >> shift) & 255u;
         }
         // after the first passes few candidates still match: a wave with none
@@ -134,7 +187,7 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
             s += h[j];
         }
         const int x = wave_scan_incl(s);
-        if (pass == 0 && __builtin_amdgcn_readlane(x, 63) <= bud) {  // everything fits
+        if (pass == 0 && forced + __builtin_amdgcn_readlane(x, 63) <= bud) {  // everything fits
             all = true;
             break;
         }
@@ -160,6 +213,7 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
             pmask = 0xffffffffu;
             break;
         }
+        if (shift == 0) break;  // every bit resolved
     }
     const uint32_t T = prefix;
     const int remaining = bud - wabove;

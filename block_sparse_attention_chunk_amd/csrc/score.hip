@@ -129,38 +129,34 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(const uint16_t *
                                                                 const float *__restrict__ cen,
                                                                 float *__restrict__ out) {
     constexpr int NS = 2 * D / 32;  // MFMA steps over 2*D features
+    args_ready(q, hq, kv.hkv, kv.seq_lens, kv.page, kv.log2page, ch.starts, ch.num, ch.max_chunks, kmin, kmax, cen,
+               out);
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = hq / kv.hkv;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, G = lane >> 4;
-    const int n = ch.starts ? ch.num[b] : (kv.seq_lens[b] + kv.page - 1) >> kv.log2page;
     float *orow = out + ((int64_t)b * kv.hkv + h) * ch.max_chunks;
-    bf16x8 bq[NS];
-    {
-        uint4 qv[NS / 2];
-#pragma unroll
-        for (int s = 0; s < NS / 2; ++s) {
-            qv[s] = make_uint4(0, 0, 0, 0);
-            if (n16 < g)
-                qv[s] = *reinterpret_cast<const uint4 *>(q + ((int64_t)b * hq + h * g + n16) * D + 32 * s + 8 * G);
-        }
-#pragma unroll
-        for (int s = 0; s < NS / 2; ++s) {
-            if constexpr (KIND == BSA_ENVELOPE) {
-                bq[s] = __builtin_bit_cast(bf16x8, split_sign(qv[s], false));
-                bq[s + NS / 2] = __builtin_bit_cast(bf16x8, split_sign(qv[s], true));
-            } else {
-                bq[s] = __builtin_bit_cast(bf16x8, qv[s]);
-                bq[s + NS / 2] = bq[s];
-            }
-        }
-    }
     const int64_t mbase = ((int64_t)b * kv.hkv + h) * ch.max_chunks * D;
-    // chunk groups of 16: wave-strided over the grid, the next group's metadata
-    // in flight while the current one is reduced
     const int stride = gridDim.x * 4;
     const int n_groups = (ch.max_chunks + 15) / 16;
+    const int first = blockIdx.x * 4 + w;
+    if (first >= n_groups) return;
+    // The row length, the query and the first metadata group are requested
+    // together: every load is unconditional and none depends on another.
+    const int *len_src = ch.starts ? ch.num : kv.seq_lens;
+    const int len = len_src[b];
+    bf16x8 bq[NS];
+    uint4 qv[NS / 2];
+    {
+        const int jq = min(n16, g - 1);  // padding columns load a real head, zeroed below
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s)
+            qv[s] = *reinterpret_cast<const uint4 *>(q + ((int64_t)b * hq + h * g + jq) * D + 32 * s + 8 * G);
+    }
+    // rows are clamped into the allocated max_chunks, not to the row length, so
+    // the first requests do not wait for it; rows past the length are scored
+    // and discarded
     auto load = [&](int grp, uint4 (&a)[NS]) {
-        const int c = min(grp * 16 + n16, n - 1);  // clamped: always a valid row
+        const int c = min(grp * 16 + n16, ch.max_chunks - 1);
         const int64_t mrow = mbase + (int64_t)c * D;
         if constexpr (KIND == BSA_ENVELOPE) {
 #pragma unroll
@@ -180,6 +176,36 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(const uint16_t *
             }
         }
     };
+    uint4 aA[NS], aB[NS];
+    load(first, aA);
+    // the length is used only from here on, so its wait follows every request
+    // above (the compiler would otherwise compute the chunk count, and wait,
+    // before issuing them)
+    int len_v = len;
+    asm volatile("" : "+v"(len_v)::"memory");
+    const int n = ch.starts ? len_v : (len_v + kv.page - 1) >> kv.log2page;
+    {
+        const uint32_t qm = n16 < g ? 0xffffffffu : 0u;  // a mask: a select would move the loads into a branch
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            qv[s].x &= qm;
+            qv[s].y &= qm;
+            qv[s].z &= qm;
+            qv[s].w &= qm;
+        }
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            if constexpr (KIND == BSA_ENVELOPE) {
+                bq[s] = __builtin_bit_cast(bf16x8, split_sign(qv[s], false));
+                bq[s + NS / 2] = __builtin_bit_cast(bf16x8, split_sign(qv[s], true));
+            } else {
+                bq[s] = __builtin_bit_cast(bf16x8, qv[s]);
+                bq[s + NS / 2] = bq[s];
+            }
+        }
+    }
+    // chunk groups of 16: wave-strided over the grid, the next group's metadata
+    // in flight while the current one is reduced
     auto score = [&](int grp, const uint4 (&araw)[NS]) {
         const int c0 = grp * 16;
         uint4 a[NS];
@@ -229,15 +255,6 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(const uint16_t *
             }
         }
     };
-    const int first = blockIdx.x * 4 + w;
-    if (first >= n_groups) return;
-    if (n <= 0) {
-        for (int grp = first; grp < n_groups; grp += stride)
-            if (lane < 16 && grp * 16 + lane < ch.max_chunks) orow[grp * 16 + lane] = -INFINITY;
-        return;
-    }
-    uint4 aA[NS], aB[NS];
-    load(first, aA);
     for (int grp = first; grp < n_groups; grp += 2 * stride) {
         load(min(grp + stride, n_groups - 1), aB);   // unconditional: exact memory counters
         score(grp, aA);

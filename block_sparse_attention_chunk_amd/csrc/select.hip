@@ -24,6 +24,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ sc
                                                         bsa_budget bud, int32_t *__restrict__ sel_idx,
                                                         int32_t *__restrict__ sel_count, int max_sel) {
     __shared__ RadixShared sh;
+    args_ready(scores, kv.hkv, kv.seq_lens, kv.page, kv.log2page, ch.max_chunks, ch.starts, ch.num, bud.mode, bud.top_k,
+               bud.tokens, bud.bos, bud.eos, bud.ratio);
     const int h = blockIdx.x, b = blockIdx.y;
     const float *row = scores + ((int64_t)b * kv.hkv + h) * ch.max_chunks;
     const int base = threadIdx.x * PER;

@@ -39,6 +39,8 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
     __shared__ float mbuf[kDecWaves * 16], lbuf[kDecWaves * 16];
     __shared__ RadixShared sh;
     __shared__ int32_t list[kFusedListCap], plist[kFusedListCap];  // logical / physical pages of this split
+    args_ready(q, hq, kv.hkv, kv.max_pages, kv.bt, kv.seq_lens, scores, bud.mode, bud.top_k, bud.tokens, bud.bos,
+               bud.eos, bud.ratio);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int g = hq / kv.hkv;
@@ -56,12 +58,12 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
     // unconditional and the memory waits stay exact)
     const bool has_bt = kv.bt != nullptr;
     const int32_t *btr = has_bt ? kv.bt + (int64_t)b * kv.max_pages : reinterpret_cast<const int32_t *>(row);
+    const int bt_mask = has_bt ? -1 : 0;  // a mask, not a select: a select would move the load into a branch
     int phys[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int c = min(base + i, mc - 1);
-        const int v = btr[c];
-        phys[i] = has_bt ? v : b * kv.max_pages + c;
+        phys[i] = (btr[c] & bt_mask) | ((b * kv.max_pages + c) & ~bt_mask);
     }
     uint4 qb[NW];
     load_q_operand<T, D>(q, hq, g, b, h, lane, qb);

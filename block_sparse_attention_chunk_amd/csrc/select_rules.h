@@ -46,16 +46,27 @@ template <int PER>
 __device__ __forceinline__ void select_keys(const float (&raw)[PER], int base, int n, const RowBudget &rb,
                                             const int32_t *starts, int L, int page, int log2page,
                                             uint32_t (&keys)[PER], int (&wts)[PER]) {
+    // straight-line selects per candidate; only the token weights of variable
+    // chunks need memory (uniform branch)
+    const int fb = rb.forced_bos ? 0 : -1, fe = rb.forced_eos ? n - 1 : -1;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int c = base + i;
-        keys[i] = 0u;
+        const bool valid = c < n;
+        const uint32_t k = (c == fb || c == fe) ? 0xffffffffu : float_key(raw[i]);
+        keys[i] = valid ? k : 0u;
         wts[i] = 1;
-        if (c < n) {
-            uint32_t k = float_key(raw[i]);
-            if ((rb.forced_bos && c == 0) || (rb.forced_eos && c == n - 1)) k = 0xffffffffu;
-            keys[i] = k;
-            if (rb.tokens) wts[i] = starts ? starts[c + 1] - starts[c] : min(page, L - (c << log2page));
+    }
+    if (rb.tokens) {
+        if (starts) {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int c = min(base + i, max(n - 1, 0));
+                wts[i] = base + i < n ? starts[c + 1] - starts[c] : 1;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) wts[i] = base + i < n ? min(page, L - ((base + i) << log2page)) : 1;
         }
     }
 }
