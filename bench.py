@@ -456,7 +456,7 @@ class LayerStackBench:
 
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_decode_replay_b1_hbm_traffic.txt")
-KERNEL_SOURCES = ["select_decode.hip", "decode_common.h", "radix_select.h", "select_rules.h"]
+KERNEL_SOURCES = ["select_decode.hip", "decode_common.h", "radix_select.h", "select_rules.h", "bsa_internal.h"]
 
 
 def kernel_source_hash():
