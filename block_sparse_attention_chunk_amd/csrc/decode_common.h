@@ -251,8 +251,10 @@ __device__ __forceinline__ void init_state(WaveState<T, D, GP> &st) {
 
 // Merge the 4 waves' states in LDS (each wave's output slice reuses its own
 // region, which no other wave touches) and write either the final output
-// (one split) or this split's partial (unnormalised o, max m, sum l).
-template <typename T, int D, int GP>
+// (one split) or this split's partial (unnormalised o, max m, sum l).  NT is
+// the workgroup size; waves from kDecWaves on hold no state and only help
+// with the merge.
+template <typename T, int D, int GP, int NT = kDecWaves * 64>
 __device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float *regions, float *mbuf, float *lbuf,
                                                  int g, int hq, int b, int h, int split, int splits,
                                                  float *__restrict__ out, float *__restrict__ part_o,
@@ -263,32 +265,34 @@ __device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float 
     l1 += __shfl_xor(l1, 32, 64);
     wave_lds_sync();  // this wave's last reads of its region are done
     float *ob = regions + w * R;
-    if (G == 0) {
-        mbuf[w * 16 + n16] = st.m_run;
-        lbuf[w * 16 + n16] = l1;
-    }
-    if constexpr (DecTraits<T, D>::kBf16) {
-        // tile dt, row 4G+i holds dim kVPL*(4G+i) + dt of head n16
-        constexpr int VPL = DecTraits<T, D>::kVPL;
-        if (n16 < g) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int d4 = 0; d4 < VPL; d4 += 4)
-                    *reinterpret_cast<float4 *>(ob + n16 * D + VPL * (4 * G + i) + d4) =
-                        make_float4(st.o[d4][i], st.o[d4 + 1][i], st.o[d4 + 2][i], st.o[d4 + 3][i]);
+    if (w < kDecWaves) {
+        if (G == 0) {
+            mbuf[w * 16 + n16] = st.m_run;
+            lbuf[w * 16 + n16] = l1;
         }
-    } else {
-        constexpr int VD = D / 64;
+        if constexpr (DecTraits<T, D>::kBf16) {
+            // tile dt, row 4G+i holds dim kVPL*(4G+i) + dt of head n16
+            constexpr int VPL = DecTraits<T, D>::kVPL;
+            if (n16 < g) {
 #pragma unroll
-        for (int j = 0; j < GP; ++j)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int dd = 0; dd < VD; ++dd) ob[j * D + VD * lane + dd] = st.acc[j][dd];
+                    for (int d4 = 0; d4 < VPL; d4 += 4)
+                        *reinterpret_cast<float4 *>(ob + n16 * D + VPL * (4 * G + i) + d4) =
+                            make_float4(st.o[d4][i], st.o[d4 + 1][i], st.o[d4 + 2][i], st.o[d4 + 3][i]);
+            }
+        } else {
+            constexpr int VD = D / 64;
+#pragma unroll
+            for (int j = 0; j < GP; ++j)
+#pragma unroll
+                for (int dd = 0; dd < VD; ++dd) ob[j * D + VD * lane + dd] = st.acc[j][dd];
+        }
     }
     __syncthreads();
     // each thread merges 4 consecutive dims of one head
     constexpr int D4 = D / 4;
-    for (int idx = threadIdx.x; idx < g * D4; idx += kDecWaves * 64) {
+    for (int idx = threadIdx.x; idx < g * D4; idx += NT) {
         const int j = idx / D4, d = (idx % D4) * 4;
         float mw[kDecWaves], M = -INFINITY;
 #pragma unroll

@@ -18,8 +18,10 @@
 // The split-0 workgroup also writes the kept list and its length when asked.
 // This removes one launch and the selection's round trips through memory from
 // every decode step; the redundant per-split selection costs a few
-// microseconds of on-chip work per workgroup, hidden behind other
-// workgroups' K/V reads at large batch.
+// microseconds of on-chip work per workgroup.  When the grid has at most one
+// workgroup per compute unit (a few sequences), that selection is the
+// critical path, so 8 waves share it; the attention still runs on the first
+// 4 waves with the unfused kernel's assignment.
 #include "decode_common.h"
 #include "radix_select.h"
 #include "select_rules.h"
@@ -27,9 +29,10 @@
 namespace bsa {
 
 constexpr int kFusedListCap = 2048;  // kept pages per workgroup
+constexpr int kSmallGrid = 256;      // workgroups: one per compute unit
 
-template <typename T, int D, int GP, int PER>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 1)
+template <typename T, int D, int GP, int PER, int NT>
+__global__ __launch_bounds__(NT, (sizeof(T) == 2 && NT == 256) ? 3 : 1)
 void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const float *__restrict__ scores,
                           bsa_budget bud, int32_t *__restrict__ sel_idx, int32_t *__restrict__ sel_count,
                           int max_sel, float scale_log2, int splits, float *__restrict__ out,
@@ -79,7 +82,7 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
     // have consecutive ranks, so one division per thread sets (slot, split)
     // and each kept page steps it
     int qs = 0, rs = 0;
-    const int cnt = radix_select_prefix_emit<256, PER>(
+    const int cnt = radix_select_prefix_emit<NT, PER>(
         keys, wts, base, n, rb.budget,
         [&](int p0) {
             qs = p0 / splits;
@@ -98,14 +101,15 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
         },
         sh);
     if (dst) {
-        for (int i = cnt + (int)threadIdx.x; i < max_sel; i += 256) dst[i] = -1;
+        for (int i = cnt + (int)threadIdx.x; i < max_sel; i += NT) dst[i] = -1;
         if (threadIdx.x == 0) sel_count[(int64_t)b * kv.hkv + h] = min(cnt, max_sel);
     }
     __syncthreads();
 
-    // this workgroup's items: local positions w, w + 4, ... of its list
+    // this workgroup's items: local positions w, w + 4, ... of its list, for
+    // the first kDecWaves waves (the others only helped with the selection)
     const int local = cnt > split ? (cnt - split + splits - 1) / splits : 0;
-    const int n_mine = local > w ? (local - w + kDecWaves - 1) / kDecWaves : 0;
+    const int n_mine = (w < kDecWaves && local > w) ? (local - w + kDecWaves - 1) / kDecWaves : 0;
     WaveState<T, D, GP> st;
     init_state(st);
     const T *kb = reinterpret_cast<const T *>(kv.k) + (int64_t)h * kv.sh;
@@ -113,25 +117,40 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
     auto slot = [&](int ib) { return min(w + kDecWaves * (ib + lane), kFusedListCap - 1); };
     auto page_of = [&](int ib) { return list[slot(ib)]; };
     auto phys_of = [&](int ib, int) { return plist[slot(ib)]; };
-    stream_pages<T, D, GP, BSA_DECODE_PD>(st, qb, kv, kb, vb, L, n_mine, page_of, phys_of, scale_log2,
-                                          regions + w * R, lane);
-    finish_workgroup<T, D, GP>(st, regions, mbuf, lbuf, g, hq, b, h, split, splits, out, part_o, part_ml);
+    if (w < kDecWaves)
+        stream_pages<T, D, GP, BSA_DECODE_PD>(st, qb, kv, kb, vb, L, n_mine, page_of, phys_of, scale_log2,
+                                              regions + w * R, lane);
+    finish_workgroup<T, D, GP, NT>(st, regions, mbuf, lbuf, g, hq, b, h, split, splits, out, part_o, part_ml);
 }
 
 template <typename T, int D, int GP>
 static void launch_sd_t(const void *q, int hq, const KvView &kv, const float *scores, const bsa_budget &bud,
                         int32_t *sel_idx, int32_t *sel_count, int max_sel, float scale_log2, int splits, float *out,
                         float *part_o, float *part_ml, hipStream_t s) {
-    dim3 grid(splits, kv.hkv, kv.batch), block(kDecWaves * 64);
-#define BSA_SD_LAUNCH(PER)                                                                                       \
-    hipLaunchKernelGGL((select_decode_kernel<T, D, GP, PER>), grid, block, 0, s, (const T *)q, hq, kv, scores, bud, \
-                       sel_idx, sel_count, max_sel, scale_log2, splits, out, part_o, part_ml)
-    if (kv.max_pages <= 256 * 8)
-        BSA_SD_LAUNCH(8);
-    else if (kv.max_pages <= 256 * 16)
-        BSA_SD_LAUNCH(16);
-    else
-        BSA_SD_LAUNCH(32);
+    dim3 grid(splits, kv.hkv, kv.batch);
+#define BSA_SD_LAUNCH(PER, NT)                                                                                    \
+    hipLaunchKernelGGL((select_decode_kernel<T, D, GP, PER, NT>), grid, dim3(NT), 0, s, (const T *)q, hq, kv, scores, \
+                       bud, sel_idx, sel_count, max_sel, scale_log2, splits, out, part_o, part_ml)
+    // A grid of at most one workgroup per compute unit is latency-bound: 8
+    // waves share the selection (half the candidates per thread), and the
+    // first 4 attend as usual.  Larger grids keep 4 waves, so 3 workgroups fit
+    // on a compute unit.
+    const int64_t wgs = (int64_t)splits * kv.hkv * kv.batch;
+    if (wgs <= kSmallGrid) {
+        if (kv.max_pages <= 512 * 4)
+            BSA_SD_LAUNCH(4, 512);
+        else if (kv.max_pages <= 512 * 8)
+            BSA_SD_LAUNCH(8, 512);
+        else
+            BSA_SD_LAUNCH(16, 512);
+    } else {
+        if (kv.max_pages <= 256 * 8)
+            BSA_SD_LAUNCH(8, 256);
+        else if (kv.max_pages <= 256 * 16)
+            BSA_SD_LAUNCH(16, 256);
+        else
+            BSA_SD_LAUNCH(32, 256);
+    }
 #undef BSA_SD_LAUNCH
 }
 
