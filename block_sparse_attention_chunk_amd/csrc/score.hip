@@ -351,15 +351,40 @@ __device__ __forceinline__ uint4 split_sign(uint4 w, bool neg) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Maximum over the 16 lanes of each 16-lane row (rotations inside the row).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
+    return v;
+}
+
+// One 16-byte piece of a 16-block metadata tile as loaded from memory (the
+// centroid needs 8 fp32 for 8 bf16 features).
 template <int KIND>
+struct TilePiece {
+    uint4 a, b;
+};
+
+// IPT staged pieces per thread; PF tiles are in flight (in registers) while
+// one is computed, so the metadata latency is covered by PF tiles of matrix
+// work.  One barrier per tile: the staging buffer and the per-head maxima are
+// double-buffered, and a tile's maxima are reduced over the heads after the
+// next tile's barrier.
+template <int KIND, int IPT>
 __global__ __launch_bounds__(512) void score_tiles_kernel(const uint16_t *__restrict__ q, int hq, int rows,
                                                           KvView kv, int n_blocks, const uint16_t *__restrict__ kmin,
                                                           const uint16_t *__restrict__ kmax,
                                                           const float *__restrict__ cen, int causal,
                                                           float *__restrict__ out) {
     constexpr int D = 128;
-    __shared__ __attribute__((aligned(16))) uint16_t feat[kBlkTile * kFeatRow];
-    __shared__ float red[8][kBlkTile];
+    constexpr int PF = IPT >= 8 ? 1 : (8 / IPT > 4 ? 4 : 8 / IPT);
+    // two staging buffers, then one 16-byte slot that absorbs the stores of
+    // threads without a piece (so staging has no branch)
+    __shared__ __attribute__((aligned(16))) uint16_t feat[2 * kBlkTile * kFeatRow + 8];
+    __shared__ float red[2][8][kBlkTile];
+    args_ready(q, hq, rows, kv.hkv, kv.page, n_blocks, kmin, kmax, cen, causal, out);
     const int t = blockIdx.x, h = blockIdx.y;
     const int g = hq / kv.hkv;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -368,19 +393,84 @@ __global__ __launch_bounds__(512) void score_tiles_kernel(const uint16_t *__rest
     const int r0 = t * kTileRows;
     const int vis = causal ? min(n_blocks, (min(r0 + kTileRows, rows) - 1) / kv.page + 1) : n_blocks;
     float *orow = out + ((int64_t)t * kv.hkv + h) * n_blocks;
+    const int64_t mbase = ((int64_t)h * n_blocks) * D;  // batch 1
+    const int ntiles16 = (vis + kBlkTile - 1) / kBlkTile;
 
-    // B operand: this wave's 64 rows (query head h*g + w), 8 k-steps of 32 features
-    bf16x8 bq[4][8];
+    // the metadata pieces of tile bt this thread stages: piece i = tid + k*nthreads
+    // (block i >> 5, 16-byte part i & 31 of its 512-byte feature row); loads
+    // are unconditional, clamped to real rows (rows past vis are discarded)
+    auto fetch = [&](int bt, TilePiece<KIND> (&v)[IPT]) {
+        bt = min(bt, max(ntiles16 - 1, 0));
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int i = min((int)threadIdx.x + k * nthreads, kBlkTile * 32 - 1);
+            const int blk = min(bt * kBlkTile + (i >> 5), max(vis - 1, 0));
+            const int part = i & 31, dpiece = part & 15;
+            if constexpr (KIND == BSA_ENVELOPE) {
+                const uint16_t *src = (part < 16 ? kmax : kmin) + mbase + (int64_t)blk * D + dpiece * 8;
+                v[k].a = *reinterpret_cast<const uint4 *>(src);
+            } else {
+                const float *src = cen + mbase + (int64_t)blk * D + dpiece * 8;
+                const float4 x0 = reinterpret_cast<const float4 *>(src)[0];
+                const float4 x1 = reinterpret_cast<const float4 *>(src)[1];
+                v[k].a = make_uint4(__float_as_uint(x0.x), __float_as_uint(x0.y), __float_as_uint(x0.z),
+                                    __float_as_uint(x0.w));
+                v[k].b = make_uint4(__float_as_uint(x1.x), __float_as_uint(x1.y), __float_as_uint(x1.z),
+                                    __float_as_uint(x1.w));
+            }
+        }
+    };
+    auto stage = [&](const TilePiece<KIND> (&v)[IPT], uint16_t *dst) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int i = (int)threadIdx.x + k * nthreads;
+            const int bl = i >> 5, part = i & 31;
+            uint4 o4;
+            if constexpr (KIND == BSA_ENVELOPE) {
+                o4 = v[k].a;
+            } else {
+                const uint32_t xw[8] = {v[k].a.x, v[k].a.y, v[k].a.z, v[k].a.w,
+                                        v[k].b.x, v[k].b.y, v[k].b.z, v[k].b.w};
+                uint16_t o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = __uint_as_float(xw[e]);
+                    const uint16_t hb = f32_to_bf16_rne(x);
+                    o[e] = part < 16 ? hb : f32_to_bf16_rne(x - bf16_to_f32(hb));
+                }
+                o4 = make_uint4(o[0] | (uint32_t(o[1]) << 16), o[2] | (uint32_t(o[3]) << 16),
+                                o[4] | (uint32_t(o[5]) << 16), o[6] | (uint32_t(o[7]) << 16));
+            }
+            uint16_t *at = i < kBlkTile * 32 ? dst + bl * kFeatRow + part * 8 : feat + 2 * kBlkTile * kFeatRow;
+            *reinterpret_cast<uint4 *>(at) = o4;
+        }
+    };
+
+    // B operand: this wave's 64 rows (query head h*g + w), 8 k-steps of 32
+    // features.  The query is requested first, then the first PF metadata
+    // tiles, so the query's wait leaves the tiles in flight.
+    uint4 qraw[4][4];
     bool rvalid[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         const int r = r0 + rt * 16 + n16;
         rvalid[rt] = r < rows;
 #pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qraw[rt][s] = *reinterpret_cast<const uint4 *>(q + ((int64_t)min(r, rows - 1) * hq + h * g + min(w, g - 1)) *
+                                                               D + 32 * s + 8 * G);
+    }
+    TilePiece<KIND> pre[PF][IPT];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) fetch(p, pre[p]);
+    bf16x8 bq[4][8];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const uint32_t m = rvalid[rt] ? 0xffffffffu : 0u;
+#pragma unroll
         for (int s = 0; s < 4; ++s) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (rvalid[rt])
-                v = *reinterpret_cast<const uint4 *>(q + ((int64_t)r * hq + h * g + w) * D + 32 * s + 8 * G);
+            uint4 v = qraw[rt][s];
+            v.x &= m, v.y &= m, v.z &= m, v.w &= m;
             if constexpr (KIND == BSA_ENVELOPE) {
                 bq[rt][s] = __builtin_bit_cast(bf16x8, split_sign(v, false));
                 bq[rt][s + 4] = __builtin_bit_cast(bf16x8, split_sign(v, true));
@@ -391,78 +481,53 @@ __global__ __launch_bounds__(512) void score_tiles_kernel(const uint16_t *__rest
         }
     }
 
-    const int64_t mbase = ((int64_t)h * n_blocks) * D;  // batch 1
-    const int ntiles16 = (vis + kBlkTile - 1) / kBlkTile;
-    for (int bt = 0; bt < ntiles16; ++bt) {
-        const int b0 = bt * kBlkTile;
-        // stage 16 blocks x 256 bf16 features
-        for (int i = threadIdx.x; i < kBlkTile * 32; i += nthreads) {
-            const int bl = i >> 5, part = i & 31;  // part: 16-byte piece of the 512-byte feature row
-            const int blk = b0 + bl;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (blk < vis) {
-                const int dpiece = part & 15;  // 8 dims
-                if constexpr (KIND == BSA_ENVELOPE) {
-                    const uint16_t *src = (part < 16 ? kmax : kmin) + mbase + (int64_t)blk * D + dpiece * 8;
-                    v = *reinterpret_cast<const uint4 *>(src);
-                } else {
-                    const float *src = cen + mbase + (int64_t)blk * D + dpiece * 8;
-                    const float4 a = reinterpret_cast<const float4 *>(src)[0];
-                    const float4 c = reinterpret_cast<const float4 *>(src)[1];
-                    const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-                    uint16_t o[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint16_t hb = f32_to_bf16_rne(x[e]);
-                        o[e] = part < 16 ? hb : f32_to_bf16_rne(x[e] - bf16_to_f32(hb));
-                    }
-                    v = make_uint4(o[0] | (uint32_t(o[1]) << 16), o[2] | (uint32_t(o[3]) << 16),
-                                   o[4] | (uint32_t(o[5]) << 16), o[6] | (uint32_t(o[7]) << 16));
-                }
-            }
-            *reinterpret_cast<uint4 *>(feat + bl * kFeatRow + part * 8) = v;
-        }
-        __syncthreads();
-        float bmax[4];
-        if (w < g) {
-            f32x4 acc[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(feat + n16 * kFeatRow + 32 * s + 8 * G);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[rt][s], acc[rt], 0, 0, 0);
-            }
-            // lane holds S^T[block 4G+i][row n16] of each row tile
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float m = -INFINITY;
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    if (rvalid[rt]) m = fmaxf(m, acc[rt][i]);
-                m = wave_max_xor(m, 1);
-                m = wave_max_xor(m, 2);
-                m = wave_max_xor(m, 4);
-                m = wave_max_xor(m, 8);
-                bmax[i] = m;
-            }
-            if (n16 == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) red[w][4 * G + i] = bmax[i];
-            }
-        }
-        __syncthreads();
+    // maxima of tile bt over the group's heads -> the output row
+    auto finalize = [&](int bt) {
         if (threadIdx.x < kBlkTile) {
-            const int blk = b0 + threadIdx.x;
+            const int blk = bt * kBlkTile + threadIdx.x;
             if (blk < vis) {
-                float m = red[0][threadIdx.x];
-                for (int j = 1; j < g; ++j) m = fmaxf(m, red[j][threadIdx.x]);
+                float m = red[bt & 1][0][threadIdx.x];
+                for (int j = 1; j < g; ++j) m = fmaxf(m, red[bt & 1][j][threadIdx.x]);
                 orow[blk] = m;
             }
         }
+    };
+    for (int bt0 = 0; bt0 < ntiles16; bt0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int bt = bt0 + p;
+            if (bt >= ntiles16) break;
+            uint16_t *fb = feat + (bt & 1) * kBlkTile * kFeatRow;
+            // stage the oldest tile in flight and reuse its registers for tile bt + PF
+            stage(pre[p], fb);
+            fetch(bt + PF, pre[p]);
+            __syncthreads();
+            if (bt > 0) finalize(bt - 1);
+            if (w < g) {
+                f32x4 acc[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(fb + n16 * kFeatRow + 32 * s + 8 * G);
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+                        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[rt][s], acc[rt], 0, 0, 0);
+                }
+                // lane holds S^T[block 4G+i][row n16] of each row tile
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float m = -INFINITY;
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) m = rvalid[rt] ? fmaxf(m, acc[rt][i]) : m;
+                    m = row16_max(m);
+                    if (n16 == 0) red[bt & 1][w][4 * G + i] = m;
+                }
+            }
+        }
     }
+    __syncthreads();
+    if (ntiles16 > 0) finalize(ntiles16 - 1);
     for (int blk = vis + threadIdx.x; blk < n_blocks; blk += nthreads) orow[blk] = -INFINITY;
 }
 
@@ -473,12 +538,27 @@ hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t t
     const int g = hq / kv.hkv;
     const int n_tiles = (rows + kTileRows - 1) / kTileRows;
     dim3 grid(n_tiles, kv.hkv), block(64 * g);
-    if (kind == BSA_ENVELOPE)
-        hipLaunchKernelGGL((score_tiles_kernel<BSA_ENVELOPE>), grid, block, 0, s, (const uint16_t *)q, hq, rows, kv,
-                           n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal, scores);
-    else
-        hipLaunchKernelGGL((score_tiles_kernel<BSA_CENTROID>), grid, block, 0, s, (const uint16_t *)q, hq, rows, kv,
-                           n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal, scores);
+    // staged pieces per thread: 512 per tile over 64g threads
+    const int need = (16 * 32 + 64 * g - 1) / (64 * g);
+#define BSA_ST(KIND, IPT)                                                                                     \
+    hipLaunchKernelGGL((score_tiles_kernel<KIND, IPT>), grid, block, 0, s, (const uint16_t *)q, hq, rows, kv, \
+                       n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal, scores)
+#define BSA_ST_K(KIND)          \
+    if (need <= 1)              \
+        BSA_ST(KIND, 1);        \
+    else if (need <= 2)         \
+        BSA_ST(KIND, 2);        \
+    else if (need <= 4)         \
+        BSA_ST(KIND, 4);        \
+    else                        \
+        BSA_ST(KIND, 8);
+    if (kind == BSA_ENVELOPE) {
+        BSA_ST_K(BSA_ENVELOPE)
+    } else {
+        BSA_ST_K(BSA_CENTROID)
+    }
+#undef BSA_ST_K
+#undef BSA_ST
     return hipGetLastError();
 }
 
