@@ -7,7 +7,7 @@
 // Aandacht", section "Methodologie" steps 1-2 (the tile score is the maximum
 // over the tile's query rows).  Selection is per KV head, so the scores of a
 // GQA group's query heads are combined by their maximum.
-#include "bsa_internal.h"
+#include "lds_dma.h"
 
 namespace bsa {
 
@@ -351,125 +351,79 @@ __device__ __forceinline__ uint4 split_sign(uint4 w, bool neg) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// max(a, b) as one instruction: fmaxf would first quiet both inputs (the
+// compiler cannot prove matrix-core results or lane moves quiet), doubling the
+// row reduction's vector work.  Operands here are scores or -inf, never NaN.
+__device__ __forceinline__ float max_nn(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Maximum over the 16 lanes of each 16-lane row (rotations inside the row).
 __device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
     return v;
 }
 
-// One 16-byte piece of a 16-block metadata tile as loaded from memory (the
-// centroid needs 8 fp32 for 8 bf16 features).
-template <int KIND>
-struct TilePiece {
-    uint4 a, b;
-};
+// Staging of metadata tiles (16 blocks x 512 bytes: envelope [kmax | kmin]
+// bf16, centroid fp32) straight from global memory into an LDS ring,
+// kStStages tiles deep.  Wave instruction u of a tile (8 of 1 KiB) fills block
+// rows 2u, 2u+1; lane l writes 16-byte slot l mod 32 of its row, and fetches
+// the logical chunk slot ^ (row mod 8), so the 16 rows one MFMA operand read
+// touches (same logical chunk) sit in 8 different bank groups of each 8-lane
+// read group.
+constexpr int kStRowBytes = 512;
+constexpr int kStTileBytes = kBlkTile * kStRowBytes;
+constexpr int kStStages = 6;
+constexpr int kStInstrs = kStTileBytes / 1024;
 
-// IPT staged pieces per thread; PF tiles are in flight (in registers) while
-// one is computed, so the metadata latency is covered by PF tiles of matrix
-// work.  One barrier per tile: the staging buffer and the per-head maxima are
-// double-buffered, and a tile's maxima are reduced over the heads after the
-// next tile's barrier.
-template <int KIND, int IPT>
-__global__ __launch_bounds__(512) void score_tiles_kernel(const uint16_t *__restrict__ q, int hq, int rows,
-                                                          KvView kv, int n_blocks, const uint16_t *__restrict__ kmin,
-                                                          const uint16_t *__restrict__ kmax,
-                                                          const float *__restrict__ cen, int causal,
-                                                          float *__restrict__ out) {
-    constexpr int D = 128;
-    constexpr int PF = IPT >= 8 ? 1 : (8 / IPT > 4 ? 4 : 8 / IPT);
-    // two staging buffers, then one 16-byte slot that absorbs the stores of
-    // threads without a piece (so staging has no branch)
-    __shared__ __attribute__((aligned(16))) uint16_t feat[2 * kBlkTile * kFeatRow + 8];
+__device__ __forceinline__ int st_slot(int row, int chunk) { return chunk ^ (row & 7); }
+
+// G waves (one per query head of the group).  Per tile: wait for this wave's
+// copies of it, one barrier, request the tile kStStages - 1 ahead into the
+// buffer everyone has just finished, then the tile's 32 MFMAs per wave, with
+// the previous tile's row maxima (vector ALU) interleaved so the matrix and
+// vector units work at the same time; the per-head maxima of the tile before
+// are combined after the next barrier.  No compiler-visible load sits in the
+// loop.  Tiles are taken in descending order, the causal ones with the most
+// blocks first.
+template <int KIND, int G>
+__global__ __launch_bounds__(64 * G) void score_tiles_kernel(const uint16_t *__restrict__ q, int hq, int rows,
+                                                             KvView kv, int n_blocks,
+                                                             const uint16_t *__restrict__ kmin,
+                                                             const uint16_t *__restrict__ kmax,
+                                                             const float *__restrict__ cen, int causal,
+                                                             float *__restrict__ out) {
+    constexpr int D = 128, PF = kStStages;
+    constexpr int NI = (kStInstrs + G - 1) / G;
+    __shared__ __attribute__((aligned(1024))) char ring[PF * kStTileBytes];
     __shared__ float red[2][8][kBlkTile];
     args_ready(q, hq, rows, kv.hkv, kv.page, n_blocks, kmin, kmax, cen, causal, out);
-    const int t = blockIdx.x, h = blockIdx.y;
-    const int g = hq / kv.hkv;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n16 = lane & 15, G = lane >> 4;
-    const int nthreads = blockDim.x;
+    const int t = gridDim.x - 1 - blockIdx.x, h = blockIdx.y;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n16 = lane & 15, G4 = lane >> 4;
     const int r0 = t * kTileRows;
     const int vis = causal ? min(n_blocks, (min(r0 + kTileRows, rows) - 1) / kv.page + 1) : n_blocks;
     float *orow = out + ((int64_t)t * kv.hkv + h) * n_blocks;
     const int64_t mbase = ((int64_t)h * n_blocks) * D;  // batch 1
     const int ntiles16 = (vis + kBlkTile - 1) / kBlkTile;
 
-    // the metadata pieces of tile bt this thread stages: piece i = tid + k*nthreads
-    // (block i >> 5, 16-byte part i & 31 of its 512-byte feature row); loads
-    // are unconditional, clamped to real rows (rows past vis are discarded)
-    auto fetch = [&](int bt, TilePiece<KIND> (&v)[IPT]) {
-        bt = min(bt, max(ntiles16 - 1, 0));
-#pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int i = min((int)threadIdx.x + k * nthreads, kBlkTile * 32 - 1);
-            const int blk = min(bt * kBlkTile + (i >> 5), max(vis - 1, 0));
-            const int part = i & 31, dpiece = part & 15;
-            if constexpr (KIND == BSA_ENVELOPE) {
-                const uint16_t *src = (part < 16 ? kmax : kmin) + mbase + (int64_t)blk * D + dpiece * 8;
-                v[k].a = *reinterpret_cast<const uint4 *>(src);
-            } else {
-                const float *src = cen + mbase + (int64_t)blk * D + dpiece * 8;
-                const float4 x0 = reinterpret_cast<const float4 *>(src)[0];
-                const float4 x1 = reinterpret_cast<const float4 *>(src)[1];
-                v[k].a = make_uint4(__float_as_uint(x0.x), __float_as_uint(x0.y), __float_as_uint(x0.z),
-                                    __float_as_uint(x0.w));
-                v[k].b = make_uint4(__float_as_uint(x1.x), __float_as_uint(x1.y), __float_as_uint(x1.z),
-                                    __float_as_uint(x1.w));
-            }
-        }
-    };
-    auto stage = [&](const TilePiece<KIND> (&v)[IPT], uint16_t *dst) {
-#pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int i = (int)threadIdx.x + k * nthreads;
-            const int bl = i >> 5, part = i & 31;
-            uint4 o4;
-            if constexpr (KIND == BSA_ENVELOPE) {
-                o4 = v[k].a;
-            } else {
-                const uint32_t xw[8] = {v[k].a.x, v[k].a.y, v[k].a.z, v[k].a.w,
-                                        v[k].b.x, v[k].b.y, v[k].b.z, v[k].b.w};
-                uint16_t o[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = __uint_as_float(xw[e]);
-                    const uint16_t hb = f32_to_bf16_rne(x);
-                    o[e] = part < 16 ? hb : f32_to_bf16_rne(x - bf16_to_f32(hb));
-                }
-                o4 = make_uint4(o[0] | (uint32_t(o[1]) << 16), o[2] | (uint32_t(o[3]) << 16),
-                                o[4] | (uint32_t(o[5]) << 16), o[6] | (uint32_t(o[7]) << 16));
-            }
-            uint16_t *at = i < kBlkTile * 32 ? dst + bl * kFeatRow + part * 8 : feat + 2 * kBlkTile * kFeatRow;
-            *reinterpret_cast<uint4 *>(at) = o4;
-        }
-    };
-
-    // B operand: this wave's 64 rows (query head h*g + w), 8 k-steps of 32
-    // features.  The query is requested first, then the first PF metadata
-    // tiles, so the query's wait leaves the tiles in flight.
-    uint4 qraw[4][4];
+    // B operand: this wave's 64 rows (query head h*G + w), 8 k-steps of 32 features
+    bf16x8 bq[4][8];
     bool rvalid[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         const int r = r0 + rt * 16 + n16;
         rvalid[rt] = r < rows;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            qraw[rt][s] = *reinterpret_cast<const uint4 *>(q + ((int64_t)min(r, rows - 1) * hq + h * g + min(w, g - 1)) *
-                                                               D + 32 * s + 8 * G);
-    }
-    TilePiece<KIND> pre[PF][IPT];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) fetch(p, pre[p]);
-    bf16x8 bq[4][8];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
         const uint32_t m = rvalid[rt] ? 0xffffffffu : 0u;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            uint4 v = qraw[rt][s];
+            uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)min(r, rows - 1) * hq + h * G + w) * D + 32 * s +
+                                                       8 * G4);
             v.x &= m, v.y &= m, v.z &= m, v.w &= m;
             if constexpr (KIND == BSA_ENVELOPE) {
                 bq[rt][s] = __builtin_bit_cast(bf16x8, split_sign(v, false));
@@ -480,55 +434,140 @@ __global__ __launch_bounds__(512) void score_tiles_kernel(const uint16_t *__rest
             }
         }
     }
+    wait_vmcnt<0>();  // the query is in registers before any copy is issued
 
-    // maxima of tile bt over the group's heads -> the output row
+    // this wave's share of tile bt into ring buffer `stage`; tiles past the
+    // last one reload the last one (they land in a buffer nobody reads)
+    auto issue = [&](int bt, int stage) {
+        bt = min(bt, ntiles16 - 1);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int u = min(w + G * i, kStInstrs - 1);  // duplicates rewrite identical bytes
+            const int row = 2 * u + (lane >> 5);
+            const int c = st_slot(row, lane & 31);
+            const int blk = min(bt * kBlkTile + row, vis - 1);
+            const char *src;
+            if constexpr (KIND == BSA_ENVELOPE)
+                src = reinterpret_cast<const char *>((c < 16 ? kmax : kmin) + mbase + (int64_t)blk * D + 8 * (c & 15));
+            else
+                src = reinterpret_cast<const char *>(cen + mbase + (int64_t)blk * D + 4 * c);
+            dma16(src, lds_addr(ring) + stage * kStTileBytes + u * 1024);
+        }
+    };
+    // per-head maxima of tile bt -> the output row (wave 0, lanes 0..15)
     auto finalize = [&](int bt) {
         if (threadIdx.x < kBlkTile) {
             const int blk = bt * kBlkTile + threadIdx.x;
             if (blk < vis) {
                 float m = red[bt & 1][0][threadIdx.x];
-                for (int j = 1; j < g; ++j) m = fmaxf(m, red[bt & 1][j][threadIdx.x]);
+#pragma unroll
+                for (int j = 1; j < G; ++j) m = fmaxf(m, red[bt & 1][j][threadIdx.x]);
                 orow[blk] = m;
             }
         }
     };
-    for (int bt0 = 0; bt0 < ntiles16; bt0 += PF) {
+
+    auto mma = [&](int stage, f32x4 (&acc)[4]) {
+        const char *fb = ring + stage * kStTileBytes + n16 * kStRowBytes;
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int bt = bt0 + p;
-            if (bt >= ntiles16) break;
-            uint16_t *fb = feat + (bt & 1) * kBlkTile * kFeatRow;
-            // stage the oldest tile in flight and reuse its registers for tile bt + PF
-            stage(pre[p], fb);
-            fetch(bt + PF, pre[p]);
-            __syncthreads();
-            if (bt > 0) finalize(bt - 1);
-            if (w < g) {
-                f32x4 acc[4];
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (KIND == BSA_ENVELOPE) {
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(fb + 16 * st_slot(n16, 4 * s + G4));
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(fb + n16 * kFeatRow + 32 * s + 8 * G);
+                for (int rt = 0; rt < 4; ++rt)
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[rt][s], acc[rt], 0, 0, 0);
+            }
+        } else {
+            // fp32 centroid dims 32s + 8G4 .. +8 -> bf16 hi (step s) and lo (step s + 4)
 #pragma unroll
-                    for (int rt = 0; rt < 4; ++rt)
-                        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[rt][s], acc[rt], 0, 0, 0);
+            for (int s = 0; s < 4; ++s) {
+                const float4 x0 = *reinterpret_cast<const float4 *>(fb + 16 * st_slot(n16, 8 * s + 2 * G4));
+                const float4 x1 = *reinterpret_cast<const float4 *>(fb + 16 * st_slot(n16, 8 * s + 2 * G4 + 1));
+                const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                uint16_t hi[8], lo[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    hi[e] = f32_to_bf16_rne(x[e]);
+                    lo[e] = f32_to_bf16_rne(x[e] - bf16_to_f32(hi[e]));
                 }
-                // lane holds S^T[block 4G+i][row n16] of each row tile
+                const uint4 ah = make_uint4(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16),
+                                            hi[4] | (uint32_t(hi[5]) << 16), hi[6] | (uint32_t(hi[7]) << 16));
+                const uint4 al = make_uint4(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16),
+                                            lo[4] | (uint32_t(lo[5]) << 16), lo[6] | (uint32_t(lo[7]) << 16));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float m = -INFINITY;
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) m = rvalid[rt] ? fmaxf(m, acc[rt][i]) : m;
-                    m = row16_max(m);
-                    if (n16 == 0) red[bt & 1][w][4 * G + i] = m;
+                for (int rt = 0; rt < 4; ++rt) {
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), bq[rt][s],
+                                                                      acc[rt], 0, 0, 0);
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), bq[rt][s + 4],
+                                                                      acc[rt], 0, 0, 0);
                 }
             }
         }
+    };
+    // lane holds S^T[block 4G4+i][row n16] of each row tile: maximum over the
+    // wave's 64 rows -> this head's slot of the tile's maxima
+    auto reduce = [&](const f32x4 (&acc)[4], int bt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) m = max_nn(m, rvalid[rt] ? acc[rt][i] : -INFINITY);
+            m = row16_max(m);
+            red[bt & 1][w][4 * G4 + i] = m;  // every lane of the row holds the same maximum
+        }
+    };
+    // the MFMAs of one tile and the row reduction of the previous one in a
+    // single scheduling region, interleaved: one MFMA, then two vector ops
+    auto interleave = [&]() {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+    };
+    int cur = 0;  // ring buffer of the next tile
+    auto top = [&](int bt) {
+        wait_vmcnt<(PF - 2) * NI>();  // this wave's copies of tile bt have landed
+        wait_lgkm0();
+        stage_barrier();  // every wave's copies too; the previous tile's buffer and maxima are free
+        issue(bt + PF - 1, cur == 0 ? PF - 1 : cur - 1);
+        if (bt >= 2) finalize(bt - 2);
+    };
+
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p) issue(p, p);
+    f32x4 accA[4], accB[4];
+    int bt = 0;
+    for (; bt + 1 < ntiles16; bt += 2) {
+        top(bt);
+        mma(cur, accA);
+        if (bt > 0) {
+            reduce(accB, bt - 1);
+            interleave();
+        }
+        cur = cur == PF - 1 ? 0 : cur + 1;
+        top(bt + 1);
+        mma(cur, accB);
+        reduce(accA, bt);
+        interleave();
+        cur = cur == PF - 1 ? 0 : cur + 1;
     }
-    __syncthreads();
-    if (ntiles16 > 0) finalize(ntiles16 - 1);
-    for (int blk = vis + threadIdx.x; blk < n_blocks; blk += nthreads) orow[blk] = -INFINITY;
+    if (bt < ntiles16) {  // an odd count: the last tile goes to accA
+        top(bt);
+        mma(cur, accA);
+        if (bt > 0) reduce(accB, bt - 1);
+        reduce(accA, bt);
+    } else {
+        reduce(accB, bt - 1);
+    }
+    wait_vmcnt<0>();  // no copy may still target LDS when the workgroup ends
+    wait_lgkm0();
+    stage_barrier();
+    if (ntiles16 >= 2) finalize(ntiles16 - 2);
+    finalize(ntiles16 - 1);
+    for (int blk = vis + threadIdx.x; blk < n_blocks; blk += 64 * G) orow[blk] = -INFINITY;
 }
 
 hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t tile_rows, const KvView &kv,
@@ -538,26 +577,22 @@ hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t t
     const int g = hq / kv.hkv;
     const int n_tiles = (rows + kTileRows - 1) / kTileRows;
     dim3 grid(n_tiles, kv.hkv), block(64 * g);
-    // staged pieces per thread: 512 per tile over 64g threads
-    const int need = (16 * 32 + 64 * g - 1) / (64 * g);
-#define BSA_ST(KIND, IPT)                                                                                     \
-    hipLaunchKernelGGL((score_tiles_kernel<KIND, IPT>), grid, block, 0, s, (const uint16_t *)q, hq, rows, kv, \
-                       n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal, scores)
-#define BSA_ST_K(KIND)          \
-    if (need <= 1)              \
-        BSA_ST(KIND, 1);        \
-    else if (need <= 2)         \
-        BSA_ST(KIND, 2);        \
-    else if (need <= 4)         \
-        BSA_ST(KIND, 4);        \
-    else                        \
-        BSA_ST(KIND, 8);
-    if (kind == BSA_ENVELOPE) {
-        BSA_ST_K(BSA_ENVELOPE)
-    } else {
-        BSA_ST_K(BSA_CENTROID)
+#define BSA_ST(G)                                                                                                   \
+    case G:                                                                                                         \
+        if (kind == BSA_ENVELOPE)                                                                                   \
+            hipLaunchKernelGGL((score_tiles_kernel<BSA_ENVELOPE, G>), grid, block, 0, s, (const uint16_t *)q, hq,   \
+                               rows, kv, n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal,     \
+                               scores);                                                                             \
+        else                                                                                                        \
+            hipLaunchKernelGGL((score_tiles_kernel<BSA_CENTROID, G>), grid, block, 0, s, (const uint16_t *)q, hq,   \
+                               rows, kv, n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal,     \
+                               scores);                                                                             \
+        break;
+    switch (g) {
+        BSA_ST(1) BSA_ST(2) BSA_ST(3) BSA_ST(4) BSA_ST(5) BSA_ST(6) BSA_ST(7) BSA_ST(8)
+    default:
+        return hipErrorInvalidValue;
     }
-#undef BSA_ST_K
 #undef BSA_ST
     return hipGetLastError();
 }

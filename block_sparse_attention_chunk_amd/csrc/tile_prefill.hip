@@ -34,7 +34,7 @@
 // the matrix cores (an all-ones A operand); bf16 -> fp16 is exact for |v| in
 // the fp16 normal range.  Keys after a row are masked
 // only in the diagonal block.
-#include "bsa_internal.h"
+#include "lds_dma.h"
 
 namespace bsa {
 
@@ -56,41 +56,6 @@ __device__ __forceinline__ int pf_swz(int row) { return (row & 3) | ((row >> 1) 
 
 // byte offset of (row, 16-byte chunk) inside a staged K or V block
 __device__ __forceinline__ int pf_off(int row, int chunk) { return row * kPfRowBytes + 16 * (chunk ^ pf_swz(row)); }
-
-// s_waitcnt vmcnt(n) alone (expcnt / lgkmcnt left unconstrained)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// s_waitcnt lgkmcnt(0) alone
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
-
-// Workgroup barrier for the staging pipeline.  __syncthreads() would also wait
-// for this wave's copies still in flight to a different buffer (vmcnt(0));
-// here every wave has already waited for exactly what the next phase reads
-// (its own copies, vmcnt; its LDS reads and writes, lgkmcnt), and the empty
-// asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void stage_barrier() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
-
-// LDS byte address of a __shared__ pointer
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// One 16-byte-per-lane copy global -> LDS (lane l to lds + 16 l).  Written as
-// an opaque statement: the compiler does not track it, so it adds no wait of
-// its own before later LDS reads of other buffers; the kernel waits for these
-// copies explicitly (vmcnt) before the barrier that publishes a buffer.  It
-// writes no register, and the compiler's own counter waits only get stricter.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
-    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
-}
 
 // Issue this wave's share of one block's copy into stage `buf` (lds byte
 // address): wave instruction u (u < 16: K rows 4u..4u+3, else V rows), lane
@@ -128,7 +93,8 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
     __shared__ __attribute__((aligned(1024))) char stage2[kPfStageBytes];
     __shared__ int blist[kPfMaxList];
     __shared__ int nblk_s;
-    const int t = blockIdx.x >> 1, half = blockIdx.x & 1, h = blockIdx.y;
+    // tiles in descending order: causal tiles with the most blocks start first
+    const int t = (gridDim.x >> 1) - 1 - (blockIdx.x >> 1), half = blockIdx.x & 1, h = blockIdx.y;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n16 = lane & 15, G4 = lane >> 4;
     const int j = h * G + w;
