@@ -318,6 +318,7 @@ class PrefillBench:
         self.ws = torch.empty((max(ops.router_workspace_bytes(nt, pc.num_kv_heads, k, rho), 1),), dtype=torch.uint8,
                               device=dev)
         self.out = torch.empty((pc.T, pc.num_q_heads, pc.head_dim), dtype=torch.float32, device=dev)
+        self.pws = torch.empty((ops.tile_prefill_workspace_bytes(self.kv, pc.T),), dtype=torch.uint8, device=dev)
         self.r = None
 
     def build_meta(self, _=0):
@@ -332,10 +333,10 @@ class PrefillBench:
                                              workspace=self.ws)
 
     def attend(self, _=0):
-        self.ops.sparse_attn_tile_prefill(self.q, self.kv, self.r["kv_idx"], out=self.out)
+        self.ops.sparse_attn_tile_prefill(self.q, self.kv, self.r["kv_idx"], out=self.out, workspace=self.pws)
 
     def dense(self, _=0):
-        self.ops.sparse_attn_tile_prefill(self.q, self.kv, None, out=self.out)
+        self.ops.sparse_attn_tile_prefill(self.q, self.kv, None, out=self.out, workspace=self.pws)
 
     def timed(self, fn, reps):
         torch = self.torch

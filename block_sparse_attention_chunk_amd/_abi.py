@@ -52,7 +52,9 @@ SIGNATURES = {
     "bsa_sparse_attn_decode": (ctypes.c_int, [_P, _i32, _KV, _CH, _P, _P, _i32, _f32, _i32, _P, _P, _sz, _P]),
     "bsa_decode_merge": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32, _P, _P]),
     "bsa_select_attn_decode": (ctypes.c_int, [_P, _i32, _KV, _P, _BG, _f32, _i32, _P, _P, _P, _i32, _P, _sz, _P]),
-    "bsa_sparse_attn_tile_prefill": (ctypes.c_int, [_P, _i32, _i32, _KV, _i32, _P, _i32, _f32, _P, _P]),
+    "bsa_tile_prefill_workspace_bytes": (ctypes.c_size_t, [_KV, _i32]),
+    "bsa_sparse_attn_tile_prefill": (ctypes.c_int, [_P, _i32, _i32, _KV, _i32, _P, _i32, _f32, _P, _P, ctypes.c_size_t,
+                                                    _P]),
     "bsa_status_string": (ctypes.c_char_p, [_i32]),
     "bsa_last_error": (ctypes.c_char_p, []),
 }

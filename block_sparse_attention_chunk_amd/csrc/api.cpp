@@ -381,9 +381,14 @@ int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, 
                                              (hipStream_t)stream));
 }
 
+size_t bsa_tile_prefill_workspace_bytes(const bsa_kv *kv, int32_t num_rows) {
+    if (!kv || num_rows < 1 || kv->num_kv_heads < 1 || kv->head_dim < 1) return 0;
+    return (size_t)num_rows * kv->num_kv_heads * kv->head_dim * 2;  // V in fp16, [rows][H_kv][D]
+}
+
 int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num_rows, const bsa_kv *kv,
                                  int32_t tile_rows, const int32_t *kv_idx, int32_t idx_stride, float softmax_scale,
-                                 float *out, void *stream) {
+                                 float *out, void *workspace, size_t workspace_bytes, void *stream) {
     bsa::KvView v;
     int rc = check_kv(kv, true, &v);
     if (rc) return rc;
@@ -403,8 +408,12 @@ int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num
     if (kv_idx && idx_stride > 1024) return fail(BSA_ERR_UNSUPPORTED, "idx_stride %d exceeds 1024", idx_stride);
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
         return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+    const size_t need = bsa_tile_prefill_workspace_bytes(kv, num_rows);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSA_ERR_WORKSPACE, "tile prefill workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     return launched(bsa::launch_tile_prefill(q, num_q_heads, num_rows, v, tile_rows, kv_idx, idx_stride,
-                                             softmax_scale, out, (hipStream_t)stream));
+                                             softmax_scale, out, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

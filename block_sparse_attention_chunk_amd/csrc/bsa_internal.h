@@ -135,6 +135,7 @@ hipError_t launch_select_decode(const void *q, int32_t hq, const KvView &kv, con
                                 const bsa_budget &bud, int32_t *sel_idx, int32_t *sel_count, int32_t max_sel,
                                 float scale, int32_t splits, float *out, void *ws, hipStream_t s);
 hipError_t launch_tile_prefill(const void *q, int32_t hq, int32_t rows, const KvView &kv, int32_t tile_rows,
-                               const int32_t *kv_idx, int32_t idx_stride, float scale, float *out, hipStream_t s);
+                               const int32_t *kv_idx, int32_t idx_stride, float scale, float *out, void *ws,
+                               hipStream_t s);
 
 }  // namespace bsa

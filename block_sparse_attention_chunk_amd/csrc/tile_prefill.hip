@@ -27,9 +27,11 @@
 // block b+2 is in flight while block b is computed.  Inside a row the 16-byte
 // chunk c is stored at position c ^ swz(row), swz taking row bits 0-1 and 3-4:
 // the 16 rows one MFMA operand read touches then hit 16 different chunk
-// positions (no bank conflicts).  V is converted bf16 -> fp16 in place by all
-// threads once its block has landed, and the V^T operand (8 keys of one dim
-// per lane) comes from row-major V with two ds_read_b64_tr_b16 (4 keys each).
+// positions (no bank conflicts).  V arrives already in fp16: a first kernel
+// converts the whole V cache once (bf16 -> fp16, into the caller's workspace),
+// instead of every workgroup converting each staged block again.  The V^T
+// operand (8 keys of one dim per lane) comes from row-major V with two
+// ds_read_b64_tr_b16 (4 keys each).
 // P is rounded to fp16 and the row sums are taken from the rounded values on
 // the matrix cores (an all-ones A operand); bf16 -> fp16 is exact for |v| in
 // the fp16 normal range.  Keys after a row are masked
@@ -65,7 +67,8 @@ __device__ __forceinline__ int pf_off(int row, int chunk) { return row * kPfRowB
 // token-major: token pos of a head starts at base + pos * row_bytes.
 template <int G>
 __device__ __forceinline__ void issue_block(char *lds_stage, const uint16_t *kbase, const uint16_t *vbase,
-                                            int64_t row_bytes, int blk, int rows, int w, int lane) {
+                                            int64_t krow_bytes, int64_t vrow_bytes, int blk, int rows, int w,
+                                            int lane) {
     constexpr int NI = (kPfInstrs + G - 1) / G;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -73,14 +76,16 @@ __device__ __forceinline__ void issue_block(char *lds_stage, const uint16_t *kba
         const int row = 4 * (u & 15) + (lane >> 4);
         const int chunk = (lane & 15) ^ pf_swz(row);
         const int pos = min(blk * kPfBlock + row, rows - 1);
-        const char *src = reinterpret_cast<const char *>(u < 16 ? kbase : vbase) + pos * row_bytes + chunk * 16;
+        const char *src = u < 16 ? reinterpret_cast<const char *>(kbase) + pos * krow_bytes + chunk * 16
+                                 : reinterpret_cast<const char *>(vbase) + pos * vrow_bytes + chunk * 16;
         dma16(src, lds_addr(lds_stage) + u * 1024);
     }
 }
 
 template <int G>
 __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__restrict__ q, int hq, int rows,
-                                                              KvView kv, const int32_t *__restrict__ kv_idx,
+                                                              KvView kv, const uint16_t *__restrict__ v16,
+                                                              const int32_t *__restrict__ kv_idx,
                                                               int idx_stride, float scale_log2,
                                                               float *__restrict__ out) {
     constexpr int NT = 64 * G;
@@ -100,8 +105,9 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
     const int j = h * G + w;
     const int rbase = t * kPfBlock + half * kPfRowsPerWave;
     const uint16_t *kbase = reinterpret_cast<const uint16_t *>(kv.k) + (int64_t)h * kv.sh;
-    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(kv.v) + (int64_t)h * kv.sh;
+    const uint16_t *vbase = v16 + (int64_t)h * kPfD;                 // fp16 V [rows][H_kv][D]
     const int64_t row_bytes = kv.st * 2;  // token-major: stride_page == 64 * stride_token (host-checked)
+    const int64_t vrow_bytes = (int64_t)kv.hkv * kPfD * 2;
 
     // the visible selected blocks: a prefix of the ascending, -1 padded row
     // (idx_stride <= kPfMaxList, host-checked); dense: blocks 0 .. t
@@ -137,32 +143,15 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
     __syncthreads();
     const int nb = nblk_s;
     auto block_at = [&](int i) { return idx ? blist[min(i, max(nb - 1, 0))] : min(i, t); };
-    auto convert_v = [&](char *buf) {  // bf16 -> fp16 in place, 8 values per 16-byte chunk
-        uint4 *v = reinterpret_cast<uint4 *>(buf + kPfBlockBytes);
-        for (int c = threadIdx.x; c < kPfBlockBytes / 16; c += NT) {
-            const uint4 x = v[c];
-            const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
-            uint32_t y[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const _Float16 lo = (_Float16)bf16_lo(wd[e]), hi = (_Float16)bf16_hi(wd[e]);
-                y[e] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
-            }
-            v[c] = make_uint4(y[0], y[1], y[2], y[3]);
-        }
-    };
 
-    // prologue: blocks 0 and 1 copied, block 0 converted.  Everything this
-    // wave loaded so far (Q included) is waited for here, so the compiler,
-    // which does not see the copies, needs no wait of its own in the loop.
+    // prologue: blocks 0 and 1 copied.  Everything this wave loaded so far (Q
+    // included) is waited for here, so the compiler, which does not see the
+    // copies, needs no wait of its own in the loop.
     if (nb > 0) {
-        issue_block<G>(stage0, kbase, vbase, row_bytes, block_at(0), rows, w, lane);
-        issue_block<G>(stage1, kbase, vbase, row_bytes, block_at(1), rows, w, lane);
+        issue_block<G>(stage0, kbase, vbase, row_bytes, vrow_bytes, block_at(0), rows, w, lane);
+        issue_block<G>(stage1, kbase, vbase, row_bytes, vrow_bytes, block_at(1), rows, w, lane);
     }
     wait_vmcnt<0>();
-    wait_lgkm0();
-    stage_barrier();
-    if (nb > 0) convert_v(stage0);
     wait_lgkm0();
     stage_barrier();
     // Per-lane LDS byte offsets, the same for every block.  The K row of MFMA
@@ -183,11 +172,11 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
         for (int dt = 0; dt < 8; ++dt)
             voff[dt] = vrow * kPfRowBytes + 16 * ((2 * dt + ((n16 >> 1) & 1)) ^ vswz) + 8 * (n16 & 1);
     }
-    // one block: bcur holds block ii (converted), bn1 receives block ii+1 (in
-    // flight), bn2 block ii+2 (issued here; last read two blocks ago)
+    // one block: bcur holds block ii, bn1 receives block ii+1 (in flight), bn2
+    // block ii+2 (issued here; last read a block ago, before the barrier)
     auto step = [&](int ii, char *bcur, char *bn1, char *bn2) {
         const int blk = block_at(ii);
-        issue_block<G>(bn2, kbase, vbase, row_bytes, block_at(ii + 2), rows, w, lane);
+        issue_block<G>(bn2, kbase, vbase, row_bytes, vrow_bytes, block_at(ii + 2), rows, w, lane);
         const char *kc = bcur;
         const char *vc = bcur + kPfBlockBytes;
         const bool diag = blk == t;
@@ -205,8 +194,6 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
                 for (int rt = 0; rt < 2; ++rt)
                     s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][st], s[kt][rt], 0, 0, 0);
             }
-            // bounds the operand reads in flight (register pressure)
-            __builtin_amdgcn_sched_barrier(0);
         }
         // online softmax, one step per block and row.  Masks only where a key
         // can be invisible (the diagonal block, the ragged last block); the
@@ -271,7 +258,6 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
                     o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[c][rt], o[dt][rt], 0, 0, 0);
-                if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // at most 4 operand reads in flight
             }
             // row sums of the rounded weights: an all-ones A operand (every
             // output row of this tile is the column sum of P^T)
@@ -281,10 +267,8 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
         }
         // block ii+1 has landed (only block ii+2's copies may be outstanding)
         // and this wave's reads of bcur are done
+        (void)bn1;
         wait_vmcnt<NI>();
-        wait_lgkm0();
-        stage_barrier();
-        convert_v(bn1);
         wait_lgkm0();
         stage_barrier();
     };
@@ -311,17 +295,40 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
     }
 }
 
+// V (bf16, cache strides) -> fp16 [rows][H_kv][D], 8 values per thread,
+// rounded to nearest even.
+__global__ __launch_bounds__(256) void v_to_fp16_kernel(KvView kv, int rows, uint16_t *__restrict__ v16) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte piece
+    const int per_row = kv.hkv * (kPfD / 8);
+    if (i >= (int64_t)rows * per_row) return;
+    const int r = (int)(i / per_row), rem = (int)(i % per_row), h = rem / (kPfD / 8), d = (rem % (kPfD / 8)) * 8;
+    const uint4 x = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(kv.v) + r * kv.st +
+                                                     h * kv.sh + d);
+    const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+    uint32_t y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const _Float16 lo = (_Float16)bf16_lo(wd[e]), hi = (_Float16)bf16_hi(wd[e]);
+        y[e] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    *reinterpret_cast<uint4 *>(v16 + (int64_t)(r * kv.hkv + h) * kPfD + d) = make_uint4(y[0], y[1], y[2], y[3]);
+}
+
 hipError_t launch_tile_prefill(const void *q, int32_t hq, int32_t rows, const KvView &kv, int32_t tile_rows,
-                               const int32_t *kv_idx, int32_t idx_stride, float scale, float *out, hipStream_t s) {
+                               const int32_t *kv_idx, int32_t idx_stride, float scale, float *out, void *ws,
+                               hipStream_t s) {
     (void)tile_rows;  // validated: == 64 == kv.page
+    uint16_t *v16 = (uint16_t *)ws;
+    const int64_t pieces = (int64_t)rows * kv.hkv * (kPfD / 8);
+    hipLaunchKernelGGL(v_to_fp16_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, kv, rows, v16);
     const int g = hq / kv.hkv;
     const int n_tiles = (rows + kPfBlock - 1) / kPfBlock;
     dim3 grid(n_tiles * 2, kv.hkv), block(64 * g);
     const float sl = scale * kLog2e;
 #define BSA_TP(G)                                                                                            \
     case G:                                                                                                  \
-        hipLaunchKernelGGL(tile_prefill_kernel<G>, grid, block, 0, s, (const uint16_t *)q, hq, rows, kv, kv_idx, \
-                           idx_stride, sl, out);                                                             \
+        hipLaunchKernelGGL(tile_prefill_kernel<G>, grid, block, 0, s, (const uint16_t *)q, hq, rows, kv, v16,    \
+                           kv_idx, idx_stride, sl, out);                                                     \
         break;
     switch (g) {
         BSA_TP(1) BSA_TP(2) BSA_TP(3) BSA_TP(4) BSA_TP(5) BSA_TP(6) BSA_TP(7) BSA_TP(8)

@@ -18,7 +18,8 @@ from ._abi import (BSA_BF16, BSA_BUDGET_RATIO, BSA_BUDGET_TOKENS, BSA_BUDGET_TOP
                    BSA_F32, BSA_META_CENTROID, BSA_META_ENVELOPE)
 
 __all__ = ["upload", "KVCache", "Chunks", "Meta", "Budget", "build_chunk_meta", "score_chunks", "select_topk",
-           "select_topk_router", "sparse_attn_decode", "sparse_attn_tile_prefill", "decode_workspace_bytes",
+           "select_topk_router", "sparse_attn_decode", "sparse_attn_tile_prefill", "tile_prefill_workspace_bytes",
+           "decode_workspace_bytes",
            "router_workspace_bytes", "decode_num_splits"]
 
 
@@ -337,18 +338,27 @@ def select_attn_decode(q: torch.Tensor, kv: KVCache, scores: torch.Tensor, budge
     return out
 
 
+def tile_prefill_workspace_bytes(kv: KVCache, num_rows: int) -> int:
+    return int(_abi.lib().bsa_tile_prefill_workspace_bytes(ctypes.byref(kv.struct()), num_rows))
+
+
 def sparse_attn_tile_prefill(q: torch.Tensor, kv: KVCache, kv_idx: Optional[torch.Tensor] = None, tile_rows: int = 64,
-                             scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bsa_sparse_attn_tile_prefill: q [T][H_q][D] bf16 -> out [T][H_q][D] float32;
-    kv_idx [n_tiles][H_kv][stride] (-1 padded) or None (dense causal)."""
+    kv_idx [n_tiles][H_kv][stride] (-1 padded) or None (dense causal).  The
+    workspace (an fp16 copy of V) is allocated when not given."""
     T, Hq, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty((max(tile_prefill_workspace_bytes(kv, T), 16),), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     stride = 0 if kv_idx is None else int(kv_idx.shape[-1])
     L = _abi.lib()
     rc = L.bsa_sparse_attn_tile_prefill(_ptr(q), Hq, T, ctypes.byref(kv.struct()), tile_rows, _ptr(kv_idx), stride,
-                                        float(scale), _ptr(out), _stream(q.device))
+                                        float(scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(q.device))
     _abi.check(rc, "bsa_sparse_attn_tile_prefill")
     return out

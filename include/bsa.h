@@ -290,12 +290,15 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
  * page_size == tile_rows == 64 and block_table NULL.  q [num_rows][H_q][D]
  * bf16; out [num_rows][H_q][D] float32.  Matrix-core kernel (bf16 Q.K^T,
  * fp16 P.V, fp32 accumulation; V must lie in the fp16 range).  Group size
- * <= 8, head_dim 128, idx_stride <= 1024.
- * Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ * <= 8, head_dim 128, idx_stride <= 1024.  workspace (16-byte aligned, >=
+ * bsa_tile_prefill_workspace_bytes(kv, num_rows)) receives an fp16 copy of V
+ * made by the call itself; calls sharing a workspace must not overlap.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
  */
+size_t bsa_tile_prefill_workspace_bytes(const bsa_kv *kv, int32_t num_rows);
 int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num_rows, const bsa_kv *kv,
                                  int32_t tile_rows, const int32_t *kv_idx, int32_t idx_stride, float softmax_scale,
-                                 float *out, void *stream);
+                                 float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Text for a status code, and the thread-local detail of the last failure. */
 const char *bsa_status_string(int32_t status);

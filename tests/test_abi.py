@@ -160,8 +160,13 @@ def test_meta_and_score_argument_checks():
 def test_tile_prefill_argument_checks():
     L = _abi.lib()
     kvt = _kv(page_size=64, stride_page=64 * 2 * 128, stride_head=128, stride_token=256, block_table=None)
-    call = lambda kv, hq=8, tile=64, stride=4, idx=FAKE: L.bsa_sparse_attn_tile_prefill(
-        FAKE, hq, 256, ctypes.byref(kv), tile, idx, stride, 0.088, FAKE, None)
+    need = L.bsa_tile_prefill_workspace_bytes(ctypes.byref(kvt), 256)
+    assert need == 256 * 2 * 128 * 2                                    # fp16 V [rows][H_kv][D]
+    call = lambda kv, hq=8, tile=64, stride=4, idx=FAKE, ws=FAKE, wsb=need: L.bsa_sparse_attn_tile_prefill(
+        FAKE, hq, 256, ctypes.byref(kv), tile, idx, stride, 0.088, FAKE, ws, wsb, None)
+    assert call(kvt, ws=None) == _abi.BSA_ERR_WORKSPACE
+    assert call(kvt, wsb=need - 1) == _abi.BSA_ERR_WORKSPACE
+    assert call(kvt, ws=FAKE + 8) == _abi.BSA_ERR_INVALID_ARG          # alignment
     assert call(_kv()) == _abi.BSA_ERR_UNSUPPORTED                    # paged with a block table
     assert call(kvt, tile=32) == _abi.BSA_ERR_UNSUPPORTED
     assert call(kvt, hq=18) == _abi.BSA_ERR_UNSUPPORTED
