@@ -263,3 +263,16 @@ def test_varchunk_centroid_topk(dev, k):
     case = synth.varchunk_decode()
     r = run_decode_case(case, dev, ops.BSA_CENTROID, ops.Budget.topk(k), check_dense=False, splits=(0, 5))
     assert np.all(r["cnt"] == k)
+
+
+@pytest.mark.parametrize("seq_len,kind_budget", [(40000, "topk"), (120000, "ratio")])
+def test_fused_long_rows(dev, seq_len, kind_budget):
+    """Rows longer than 2048 pages: the fused kernel's wider per-thread
+    candidate sets (one sequence, so the 8-wave selection) against the oracle
+    and, bit for bit, against the two-call path."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(17, batch=1, seq_lens=[seq_len], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                             needles=12, name=f"long-{seq_len}")
+    budget = ops.Budget.topk(300) if kind_budget == "topk" else ops.Budget.ratio_budget(1 / 16, 1, 1)
+    forced = () if kind_budget == "topk" else ("bos", "eos")
+    run_decode_case(case, dev, ops.BSA_ENVELOPE, budget, forced=forced, splits=(0, 7), check_dense=False)
