@@ -230,3 +230,28 @@ def test_tile_attention_group_sizes(dev, g):
     de = max_abs(_np(dout), dref)
     assert de <= ATTN_ABS["bf16"], de
     log(f"  ok: sparse err {e:.2e}, dense err {de:.2e}")
+
+
+@pytest.mark.parametrize("g", [1, 3, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_tile_scores_group_sizes(dev, g, causal):
+    """Tile scores (both backbones) for several GQA group sizes -- different
+    copy shares per wave in the staged pipeline -- causal and not, on a
+    ragged 1,500-token prefill (24 tiles, more than one 16-block group)."""
+    from block_sparse_attention_chunk_amd import ops
+    pc = synth.router_prefill(cid=120 + g, T=1500, num_q_heads=2 * g, num_kv_heads=2, k=3, groups=4,
+                              tied_groups=(1,))
+    kv = ops.KVCache(ops.upload(pc.k, dev), ops.upload(pc.v, dev),
+                     torch.tensor([pc.T], dtype=torch.int32, device=dev), pc.block, token_major=True)
+    q = ops.upload(pc.q, dev)
+    meta = ops.build_chunk_meta(kv)
+    omin, omax, ocen = block_meta_oracle(pc)
+    for kind, okind in ((ops.BSA_ENVELOPE, oracle.ENVELOPE), (ops.BSA_CENTROID, oracle.CENTROID)):
+        log(f"tile scores g={g} causal={causal} kind={kind}")
+        ts = _np(ops.score_chunks(q, kv, meta, kind, rows_per_query=64, causal=causal))
+        ots, oden = oracle.tile_scores(pc.q, (omin, omax, ocen), okind, num_kv_heads=2, tile_rows=64,
+                                       block_size=64, causal=causal)
+        vis = np.isfinite(ots)
+        assert np.array_equal(np.isfinite(ts), vis)
+        err = np.abs(ts[vis] - ots[vis]) / oden[vis]
+        assert err.max() <= SCORE_REL, err.max()
