@@ -2,7 +2,8 @@
 selection on the same fp32 scores: the kept sets must be identical (the
 selection is an exact function of its scores).  Rows of 300, 2048 and 5000
 chunks exercise both workgroup sizes; every budget mode; rows of equal
-scores; token weights from fixed pages with a short last page."""
+scores; token weights from fixed pages with a short last page.  The fused
+selection + decode entry point must keep the same lists."""
 import numpy as np
 import pytest
 
@@ -70,8 +71,19 @@ def test_selection_with_ties_is_exact(dev, n_max, mode):
         bud = ops.Budget.ratio_budget(0.125, bos, 1)
         ref = oracle.select(sc.astype(np.float64), n, oracle.RATIO, ratio=0.125, bos=bos, eos=1,
                             max_sel=bud.max_selected(n_max))
-    sel, cnt = ops.select_topk(torch.tensor(sc, device=dev), kv, bud)
+    scores = torch.tensor(sc, device=dev)
+    sel, cnt = ops.select_topk(scores, kv, bud)
+    # the fused selection + attention writes the same kept list: a small grid
+    # (8 waves share the selection) and a large one (4 waves)
+    q = torch.zeros((B, H, 64), dtype=torch.bfloat16, device=dev)
+    fused = []
+    for splits in (0, 64):
+        fsel, fcnt = torch.full_like(sel, -7), torch.full_like(cnt, -7)
+        ops.select_attn_decode(q, kv, scores, bud, num_splits=splits, sel_idx=fsel, sel_count=fcnt)
+        fused.append((splits, fsel, fcnt))
     torch.cuda.synchronize()
+    for splits, fsel, fcnt in fused:
+        assert torch.equal(fsel, sel) and torch.equal(fcnt, cnt), f"fused selection differs (splits={splits})"
     sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
     rsel, rcnt = ref
     assert np.array_equal(cnt, rcnt)
