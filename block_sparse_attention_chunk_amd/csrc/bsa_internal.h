@@ -52,6 +52,39 @@ __device__ __forceinline__ float max_across_rows16(float v) {
     return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
 }
 
+// Sum over lanes l, l^16, l^32, l^48, the same way.
+__device__ __forceinline__ float sum_across_rows16(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = __int_as_float(a[0]) + __int_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
+// Maximum and sum over all 64 lanes of a wave, in every lane: DPP shifts
+// inside each 16-lane row, then rows combined (lane 63 ends with the total),
+// broadcast with readlane.  No LDS round trip.
+#define BSA_DPP_F(x, ctrl, rmask, ident) \
+    __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(x), ctrl, rmask, 0xf, false))
+__device__ __forceinline__ float wave_max_all(float x) {
+    x = fmaxf(x, BSA_DPP_F(x, 0x111, 0xf, -INFINITY));  // row_shr:1
+    x = fmaxf(x, BSA_DPP_F(x, 0x112, 0xf, -INFINITY));  // row_shr:2
+    x = fmaxf(x, BSA_DPP_F(x, 0x114, 0xf, -INFINITY));  // row_shr:4
+    x = fmaxf(x, BSA_DPP_F(x, 0x118, 0xf, -INFINITY));  // row_shr:8
+    x = fmaxf(x, BSA_DPP_F(x, 0x142, 0xa, -INFINITY));  // row_bcast:15
+    x = fmaxf(x, BSA_DPP_F(x, 0x143, 0xc, -INFINITY));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ float wave_sum_all(float x) {
+    x += BSA_DPP_F(x, 0x111, 0xf, 0.f);
+    x += BSA_DPP_F(x, 0x112, 0xf, 0.f);
+    x += BSA_DPP_F(x, 0x114, 0xf, 0.f);
+    x += BSA_DPP_F(x, 0x118, 0xf, 0.f);
+    x += BSA_DPP_F(x, 0x142, 0xa, 0.f);
+    x += BSA_DPP_F(x, 0x143, 0xc, 0.f);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+#undef BSA_DPP_F
+
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

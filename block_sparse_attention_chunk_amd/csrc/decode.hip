@@ -199,13 +199,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(int splits, const floa
         __builtin_amdgcn_sched_barrier(0);  // every load of the batch is in flight before the first wait
         if (s0 == 0) {
             const float m = lane < splits ? ml.x : -INFINITY;
-            float M = m;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+            const float M = wave_max_all(m);
             f = m == -INFINITY ? 0.f : exp2f(m - M);
-            lw = lane < splits ? f * ml.y : 0.f;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o, 64);
+            lw = wave_sum_all(lane < splits ? f * ml.y : 0.f);
         }
         // split s's weight sits in lane s (0 for lanes >= splits)
 #pragma unroll

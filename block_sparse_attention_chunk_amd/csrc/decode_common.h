@@ -261,8 +261,7 @@ __device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float 
                                                  float *__restrict__ part_ml) {
     constexpr int R = region_floats<D, GP>();
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, G = lane >> 4;
-    float l1 = st.l_run + __shfl_xor(st.l_run, 16, 64);
-    l1 += __shfl_xor(l1, 32, 64);
+    const float l1 = sum_across_rows16(st.l_run);
     wave_lds_sync();  // this wave's last reads of its region are done
     float *ob = regions + w * R;
     if (w < kDecWaves) {
