@@ -39,7 +39,6 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 }
 
 // ---- wave-level helpers (wave64) --------------------------------------------
-__device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
 // Max over lanes l, l^16, l^32, l^48 (the same position in the wave's four
 // 16-lane rows) with the gfx950 row-swap instructions: permlane16_swap of a

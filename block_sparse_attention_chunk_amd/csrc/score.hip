@@ -110,6 +110,24 @@ __global__ __launch_bounds__(256) void score_decode_kernel(const T *__restrict__
     out[orow] = best;
 }
 
+// max(a, b) as one instruction: fmaxf would first quiet both inputs (the
+// compiler cannot prove matrix-core results or lane moves quiet), doubling the
+// row reduction's vector work.  Operands here are scores or -inf, never NaN.
+__device__ __forceinline__ float max_nn(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Maximum over the 16 lanes of each 16-lane row (rotations inside the row).
+__device__ __forceinline__ float row16_max(float v) {
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
+    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
+    return v;
+}
+
 // Decode on the matrix cores (bf16 caches): one wave scores 16 chunks for the
 // whole GQA group.  S[chunk][head] = sum_f A[chunk][f] * B[f][head] over 2*D
 // features: envelope A = [kmax | kmin], B = [q+ ; q-] (q+ and q- are exact in
@@ -241,10 +259,7 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(const uint16_t *
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float v = n16 < g ? acc[i] : -INFINITY;
-            v = wave_max_xor(v, 1);
-            v = wave_max_xor(v, 2);
-            v = wave_max_xor(v, 4);
-            v = wave_max_xor(v, 8);
+            v = row16_max(v);
             m[i] = v;
         }
         if (n16 == 0) {
@@ -350,24 +365,6 @@ __device__ __forceinline__ uint4 split_sign(uint4 w, bool neg) {
         o[i] = neg ? (in[i] & spread) : (in[i] & ~spread);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-// max(a, b) as one instruction: fmaxf would first quiet both inputs (the
-// compiler cannot prove matrix-core results or lane moves quiet), doubling the
-// row reduction's vector work.  Operands here are scores or -inf, never NaN.
-__device__ __forceinline__ float max_nn(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-
-// Maximum over the 16 lanes of each 16-lane row (rotations inside the row).
-__device__ __forceinline__ float row16_max(float v) {
-    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
-    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
-    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
-    v = max_nn(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
-    return v;
 }
 
 // Staging of metadata tiles (16 blocks x 512 bytes: envelope [kmax | kmin]
