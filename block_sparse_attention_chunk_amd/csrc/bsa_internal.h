@@ -106,31 +106,6 @@ __device__ __forceinline__ void args_ready(const A &...a) {
     (arg_ready(a), ...);
 }
 
-// ---- block-wide inclusive scans over 256 threads (4 waves) ------------------
-// Returns the inclusive prefix of v over threadIdx.x; *total gets the block sum.
-// `scratch` needs 8 ints of shared memory.  All 256 threads must call it.
-__device__ __forceinline__ int block_scan_incl_256(int v, int *scratch, int *total) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) scratch[wid] = x;
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        int s = scratch[w];
-        if (w < wid) off += s;
-        tot += s;
-    }
-    __syncthreads();
-    *total = tot;
-    return x + off;
-}
-
 // ---- launchers (defined in the .hip files) -----------------------------------
 struct KvView {
     const void *k, *v;
