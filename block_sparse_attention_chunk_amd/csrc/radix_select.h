@@ -94,10 +94,12 @@ __device__ __forceinline__ void block_scan_pair(int &a, int &b, RadixShared &sh,
 // in order; for a kept candidate, pos is its rank in ascending index order.  A
 // thread's kept candidates take consecutive ranks: begin(p) is called once per
 // thread, before its first emit, with the rank its first kept candidate gets
-// (or would get).  The total weight must stay below 2^31.
+// (or would get).  The total weight must stay below 2^31.  `unit` (uniform):
+// every weight is 1, so the number of ties kept at the cut follows from the
+// counts alone, without a search and its barrier.
 template <int NT, int PER, typename Begin, typename Emit>
 __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[PER], const int (&wts)[PER], int base,
-                                                        int n, int64_t budget, Begin begin, Emit emit,
+                                                        int n, int64_t budget, bool unit, Begin begin, Emit emit,
                                                         RadixShared &sh) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, sub = wid & 1;
@@ -236,21 +238,27 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
     a -= gtc | (eqc << 16);
     b -= eqw;
     int gt_before = a & 0xffff, eq_before = a >> 16;
-    // the first candidate == T that no longer fits: its tie rank is the number
-    // of ties kept (none such: every tie is kept).  At most one thread finds it.
-    int hit = -1;
-    {
-        int ce = eq_before, r = b;
+    int e_sel;
+    if (unit) {
+        e_sel = min(ta >> 16, remaining);  // ties kept in index order while they fit
+    } else {
+        // the first candidate == T that no longer fits: its tie rank is the
+        // number of ties kept (none such: every tie is kept).  At most one
+        // thread finds it.
+        int hit = -1;
+        {
+            int ce = eq_before, r = b;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            hit = (eq[i] && r <= remaining && r + wts[i] > remaining) ? ce : hit;
-            r += eq[i] ? wts[i] : 0;
-            ce += eq[i] ? 1 : 0;
+            for (int i = 0; i < PER; ++i) {
+                hit = (eq[i] && r <= remaining && r + wts[i] > remaining) ? ce : hit;
+                r += eq[i] ? wts[i] : 0;
+                ce += eq[i] ? 1 : 0;
+            }
         }
+        if (hit >= 0) sh.esel = hit;
+        __syncthreads();
+        e_sel = sh.esel < 0 ? (ta >> 16) : sh.esel;
     }
-    if (hit >= 0) sh.esel = hit;
-    __syncthreads();
-    const int e_sel = sh.esel < 0 ? (ta >> 16) : sh.esel;
     begin(gt_before + min(eq_before, e_sel));
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -267,9 +275,10 @@ __device__ __forceinline__ int radix_select_prefix_emit(const uint32_t (&keys)[P
 // returns min(count, dst_cap).
 template <int NT, int PER>
 __device__ __forceinline__ int radix_select_prefix(const uint32_t (&keys)[PER], const int (&wts)[PER], int base,
-                                                   int n, int64_t budget, int *dst, int dst_cap, RadixShared &sh) {
+                                                   int n, int64_t budget, bool unit, int *dst, int dst_cap,
+                                                   RadixShared &sh) {
     const int total = radix_select_prefix_emit<NT, PER>(
-        keys, wts, base, n, budget, [](int) {}, [&](bool keep, int pos, int idx, int) {
+        keys, wts, base, n, budget, unit, [](int) {}, [&](bool keep, int pos, int idx, int) {
             if (keep && pos < dst_cap) dst[pos] = idx;
         }, sh);
     return min(total, dst_cap);

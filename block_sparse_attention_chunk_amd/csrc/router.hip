@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NT) void router_topk_kernel(const float *__restrict
         wts[i] = 1;
         if (base + i < n) skeys[base + i] = keys[i];
     }
-    const int cnt = radix_select_prefix<NT, kRtPer>(keys, wts, base, n, want, sel, kMaxList, sh);
+    const int cnt = radix_select_prefix<NT, kRtPer>(keys, wts, base, n, want, true, sel, kMaxList, sh);
     __syncthreads();
     int n2 = 1;
     while (n2 < cnt) n2 <<= 1;

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ sc
     select_keys<PER>(raw, base, n, rb, ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr, L,
                          kv.page, kv.log2page, keys, wts);
     int32_t *dst = sel_idx + ((int64_t)b * kv.hkv + h) * max_sel;
-    const int cnt = radix_select_prefix<NT, PER>(keys, wts, base, n, rb.budget, dst, max_sel, sh);
+    const int cnt = radix_select_prefix<NT, PER>(keys, wts, base, n, rb.budget, !rb.tokens, dst, max_sel, sh);
     for (int i = cnt + threadIdx.x; i < max_sel; i += NT) dst[i] = -1;
     if (threadIdx.x == 0) sel_count[(int64_t)b * kv.hkv + h] = cnt;
 }

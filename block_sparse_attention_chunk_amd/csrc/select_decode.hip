@@ -83,7 +83,7 @@ void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const floa
     // and each kept page steps it
     int qs = 0, rs = 0;
     const int cnt = radix_select_prefix_emit<NT, PER>(
-        keys, wts, base, n, rb.budget,
+        keys, wts, base, n, rb.budget, !rb.tokens,
         [&](int p0) {
             qs = p0 / splits;
             rs = p0 - qs * splits;
