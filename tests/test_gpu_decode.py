@@ -276,3 +276,36 @@ def test_fused_long_rows(dev, seq_len, kind_budget):
     budget = ops.Budget.topk(300) if kind_budget == "topk" else ops.Budget.ratio_budget(1 / 16, 1, 1)
     forced = () if kind_budget == "topk" else ("bos", "eos")
     run_decode_case(case, dev, ops.BSA_ENVELOPE, budget, forced=forced, splits=(0, 7), check_dense=False)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_empty_and_tiny_sequences(dev, fused):
+    """Degenerate rows: a sequence with no cached token (no chunk to keep: the
+    softmax over an empty set is 0/0, NaN, as in the oracle), a one-token
+    sequence and budgets larger than a row (every chunk kept)."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(61, batch=4, seq_lens=[0, 100, 1, 37], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                             name="edge")
+    kv, _ = gpu_kv(case, dev)
+    q = ops.upload(case.q, dev)
+    meta = ops.build_chunk_meta(kv)
+    scores = ops.score_chunks(q, kv, meta, ops.BSA_ENVELOPE)
+    budget = ops.Budget.topk(3)
+    if fused:
+        sel = torch.full((4, 2, 3), -7, dtype=torch.int32, device=dev)
+        cnt = torch.full((4, 2), -7, dtype=torch.int32, device=dev)
+        out = ops.select_attn_decode(q, kv, scores, budget, num_splits=2, sel_idx=sel, sel_count=cnt)
+    else:
+        sel, cnt = ops.select_topk(scores, kv, budget)
+        out = ops.sparse_attn_decode(q, kv, sel, cnt, num_splits=2)
+    torch.cuda.synchronize()
+    sc, sel, cnt, out = _np(scores), _np(sel), _np(cnt), _np(out)
+    assert np.all(sc[0] == -np.inf)                              # no chunk in the empty row
+    assert np.array_equal(cnt, [[0, 0], [3, 3], [1, 1], [3, 3]])
+    assert np.all(sel[0] == -1) and np.all(sel[2, :, 1:] == -1)
+    rsel, rcnt = oracle_select(sc.astype(np.float64), case, budget)
+    assert np.array_equal(cnt, rcnt)
+    oc = oracle_cache(case)
+    ref = oracle.decode_attn(case.q, oc, sel, cnt)
+    assert np.all(np.isnan(out[0])) and np.all(np.isnan(ref[0]))
+    assert max_abs(out[1:], ref[1:]) <= ATTN_ABS[case.dtype]
