@@ -403,6 +403,8 @@ int bsa_sparse_attn_tile_prefill(const void *q, int32_t num_q_heads, int32_t num
         return fail(BSA_ERR_UNSUPPORTED, "tile prefill supports 64-row tiles over 64-token blocks");
     if (kv->stride_page != 64 * kv->stride_token)
         return fail(BSA_ERR_UNSUPPORTED, "tile prefill needs a token-major cache (stride_page == 64 * stride_token)");
+    if (kv->stride_token >= (int64_t(1) << 24))  // 64 rows of 2-byte elements stay within 32-bit offsets
+        return fail(BSA_ERR_UNSUPPORTED, "tile prefill needs stride_token < 2^24 elements");
     if (num_rows < 1) return fail(BSA_ERR_INVALID_ARG, "num_rows must be >= 1");
     if (kv_idx && idx_stride < 1) return fail(BSA_ERR_INVALID_ARG, "idx_stride must be >= 1");
     if (kv_idx && idx_stride > 1024) return fail(BSA_ERR_UNSUPPORTED, "idx_stride %d exceeds 1024", idx_stride);

@@ -47,4 +47,11 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
     __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base plus a 32-bit per-lane byte offset
+// (the scalar-base address form: no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16_sbase(const void *base, uint32_t off, uint32_t lds) {
+    __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds)
+                     : "memory", "m0");
+}
+
 }  // namespace bsa

@@ -25,9 +25,13 @@
 // (global_load_lds, 16 bytes a lane, 1 KiB = 4 rows of 256 bytes per wave
 // instruction), three blocks deep, so no staging registers are needed and
 // block b+2 is in flight while block b is computed.  Inside a row the 16-byte
-// chunk c is stored at position c ^ swz(row), swz taking row bits 0-1 and 3-4:
-// the 16 rows one MFMA operand read touches then hit 16 different chunk
-// positions (no bank conflicts).  V arrives already in fp16: a first kernel
+// chunk c is stored at position c ^ swz(row), swz a bijection of row bits
+// 0, 1, 3 and 4 (a 256-byte row spans the 64 LDS banks once).  A K operand read
+// touches 16 rows (those four bits) at one chunk, so its 16 lanes land on 16
+// different positions.  A transposed V read makes each half-wave touch 8 rows
+// (bits 0, 1 and 3, or 0, 1 and 4 with 3 fixed) at one 32-byte chunk pair; swz
+// bits 1-3 are row bits 0, 1 and (3 xor 4), so those 8 pieces fill the 8 pair
+// positions of the bank line.  V arrives already in fp16: a first kernel
 // converts the whole V cache once (bf16 -> fp16, into the caller's workspace),
 // instead of every workgroup converting each staged block again.  The V^T
 // operand (8 keys of one dim per lane) comes from row-major V with two
@@ -54,25 +58,36 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) fp16x4_raw lds_f16x4_t;
 
-__device__ __forceinline__ int pf_swz(int row) { return (row & 3) | ((row >> 1) & 12); }
-
-// byte offset of (row, 16-byte chunk) inside a staged K or V block
-__device__ __forceinline__ int pf_off(int row, int chunk) { return row * kPfRowBytes + 16 * (chunk ^ pf_swz(row)); }
+__device__ __forceinline__ int pf_swz(int row) {
+    return ((row >> 4) & 1) | ((row & 3) << 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 3);
+}
 
 // Issue this wave's share of one block's copy into stage `buf` (lds byte
 // address): wave instruction u (u < 16: K rows 4u..4u+3, else V rows), lane
 // l writes row 4(u mod 16) + l/16 at chunk position l mod 16, so it loads
-// chunk (l mod 16) ^ swz(row).  Rows past the end clamp onto the last row
-// (those keys are masked).  Every wave issues the same count.  The cache is
-// token-major: token pos of a head starts at base + pos * row_bytes.
+// chunk (l mod 16) ^ swz(row).  Every wave issues the same count.  The cache
+// is token-major: token pos of a head starts at base + pos * row_bytes.
+// A block inside the sequence is copied from a wave-uniform block base plus
+// the lane offsets of `coff` (fixed per wave and instruction); the ragged last
+// block clamps rows past the end onto the last row (those keys are masked).
 template <int G>
 __device__ __forceinline__ void issue_block(char *lds_stage, const uint16_t *kbase, const uint16_t *vbase,
-                                            int64_t krow_bytes, int64_t vrow_bytes, int blk, int rows, int w,
-                                            int lane) {
+                                            int64_t krow_bytes, int64_t vrow_bytes, const uint32_t *coff, int blk,
+                                            int rows, int w, int lane) {
     constexpr int NI = (kPfInstrs + G - 1) / G;
+    if ((blk + 1) * kPfBlock <= rows) {
+        const char *kb = reinterpret_cast<const char *>(kbase) + (int64_t)blk * kPfBlock * krow_bytes;
+        const char *vb = reinterpret_cast<const char *>(vbase) + (int64_t)blk * kPfBlock * vrow_bytes;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int u = min(w + G * i, kPfInstrs - 1);  // duplicates rewrite identical bytes
+            dma16_sbase(u < 16 ? kb : vb, coff[i], lds_addr(lds_stage) + u * 1024);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int u = min(w + G * i, kPfInstrs - 1);  // duplicates rewrite identical bytes
+        const int u = min(w + G * i, kPfInstrs - 1);
         const int row = 4 * (u & 15) + (lane >> 4);
         const int chunk = (lane & 15) ^ pf_swz(row);
         const int pos = min(blk * kPfBlock + row, rows - 1);
@@ -142,32 +157,43 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
                         (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
     __syncthreads();
     const int nb = nblk_s;
-    auto block_at = [&](int i) { return idx ? blist[min(i, max(nb - 1, 0))] : min(i, t); };
+    auto block_at = [&](int i) {
+        return __builtin_amdgcn_readfirstlane(idx ? blist[min(i, max(nb - 1, 0))] : min(i, t));
+    };
+    // lane byte offsets of this wave's copy instructions inside a block
+    // (64 rows of either cache fit in 32 bits: host-checked)
+    uint32_t coff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int u = min(w + G * i, kPfInstrs - 1);
+        const int row = 4 * (u & 15) + (lane >> 4);
+        const int chunk = (lane & 15) ^ pf_swz(row);
+        coff[i] = (uint32_t)(row * (u < 16 ? row_bytes : vrow_bytes) + chunk * 16);
+    }
 
     // prologue: blocks 0 and 1 copied.  Everything this wave loaded so far (Q
     // included) is waited for here, so the compiler, which does not see the
     // copies, needs no wait of its own in the loop.
     if (nb > 0) {
-        issue_block<G>(stage0, kbase, vbase, row_bytes, vrow_bytes, block_at(0), rows, w, lane);
-        issue_block<G>(stage1, kbase, vbase, row_bytes, vrow_bytes, block_at(1), rows, w, lane);
+        issue_block<G>(stage0, kbase, vbase, row_bytes, vrow_bytes, coff, block_at(0), rows, w, lane);
+        issue_block<G>(stage1, kbase, vbase, row_bytes, vrow_bytes, coff, block_at(1), rows, w, lane);
     }
     wait_vmcnt<0>();
     wait_lgkm0();
     stage_barrier();
     // Per-lane LDS byte offsets, the same for every block.  The K row of MFMA
-    // row n16 in tile kt is 32(kt>>1) + 4(kt&1) + krow_lo, whose swizzle is
-    // n16 whatever kt is, so chunk 4st + G4 sits at 4(st ^ (n16>>2)) +
-    // (G4 ^ (n16&3)).  The V rows read by lane (n16, G4) are
-    // 32c + 8G4 + 4hh + (n16>>2), swizzle (n16>>2) | (G4<<2) whatever c and hh
-    // are; the lane's 8-byte piece of dims 16dt + 4(n16&3) is chunk
-    // 2dt + ((n16>>1)&1), half n16&1.
+    // row n16 in tile kt is 32(kt>>1) + 4(kt&1) + krow_lo and the V rows read
+    // by lane (n16, G4) are 32c + 8G4 + 4hh + (n16>>2): the swizzle ignores
+    // row bits 2 and 5, so it is that of krow_lo, or of 8G4 + (n16>>2),
+    // whatever kt, c and hh are.  The lane's 8-byte piece of V dims
+    // 16dt + 4(n16&3) is chunk 2dt + ((n16>>1)&1), half n16&1.
     const int krow_lo = 8 * (n16 >> 2) + (n16 & 3);
     int koff[4], voff[8];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) koff[st] = krow_lo * kPfRowBytes + 16 * (4 * (st ^ (n16 >> 2)) + (G4 ^ (n16 & 3)));
+    for (int st = 0; st < 4; ++st) koff[st] = krow_lo * kPfRowBytes + 16 * ((4 * st + G4) ^ pf_swz(krow_lo));
     {
-        const int vswz = (n16 >> 2) | (G4 << 2);
         const int vrow = 8 * G4 + (n16 >> 2);
+        const int vswz = pf_swz(vrow);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
             voff[dt] = vrow * kPfRowBytes + 16 * ((2 * dt + ((n16 >> 1) & 1)) ^ vswz) + 8 * (n16 & 1);
@@ -176,7 +202,7 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
     // block ii+2 (issued here; last read a block ago, before the barrier)
     auto step = [&](int ii, char *bcur, char *bn1, char *bn2) {
         const int blk = block_at(ii);
-        issue_block<G>(bn2, kbase, vbase, row_bytes, vrow_bytes, block_at(ii + 2), rows, w, lane);
+        issue_block<G>(bn2, kbase, vbase, row_bytes, vrow_bytes, coff, block_at(ii + 2), rows, w, lane);
         const char *kc = bcur;
         const char *vc = bcur + kPfBlockBytes;
         const bool diag = blk == t;

@@ -290,7 +290,8 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
  * page_size == tile_rows == 64 and block_table NULL.  q [num_rows][H_q][D]
  * bf16; out [num_rows][H_q][D] float32.  Matrix-core kernel (bf16 Q.K^T,
  * fp16 P.V, fp32 accumulation; V must lie in the fp16 range).  Group size
- * <= 8, head_dim 128, idx_stride <= 1024.  workspace (16-byte aligned, >=
+ * <= 8, head_dim 128, idx_stride <= 1024, stride_token < 2^24 elements.
+ * workspace (16-byte aligned, >=
  * bsa_tile_prefill_workspace_bytes(kv, num_rows)) receives an fp16 copy of V
  * made by the call itself; calls sharing a workspace must not overlap.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
