@@ -371,15 +371,15 @@ __device__ __forceinline__ uint4 split_sign(uint4 w, bool neg) {
 // bf16, centroid fp32) straight from global memory into an LDS ring,
 // kStStages tiles deep.  Wave instruction u of a tile (8 of 1 KiB) fills block
 // rows 2u, 2u+1; lane l writes 16-byte slot l mod 32 of its row, and fetches
-// the logical chunk slot ^ (row mod 8), so the 16 rows one MFMA operand read
-// touches (same logical chunk) sit in 8 different bank groups of each 8-lane
-// read group.
+// the logical chunk slot ^ (row mod 16), so the 16 rows one MFMA operand read
+// touches (same logical chunk) sit at 16 different 16-byte positions of the
+// 256-byte bank line: a 16-lane read is free of bank conflicts.
 constexpr int kStRowBytes = 512;
 constexpr int kStTileBytes = kBlkTile * kStRowBytes;
 constexpr int kStStages = 6;
 constexpr int kStInstrs = kStTileBytes / 1024;
 
-__device__ __forceinline__ int st_slot(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int st_slot(int row, int chunk) { return chunk ^ (row & 15); }
 
 // G waves (one per query head of the group).  Per tile: wait for this wave's
 // copies of it, one barrier, request the tile kStStages - 1 ahead into the
