@@ -27,7 +27,10 @@ Extra records in the same JSON line: the same layer with 16 sequences at
 4 KV heads, k = 32, rho = 2) with its MFMA utilisation, and the same router
 at 32,768 and 65,536 tokens; a 48-layer decode step (48 replay-shaped layers
 with their own caches, one HIP graph) at 1 and 16 sequences; with --extra
-also the seven ratios of the 8K-32K batched workload, both scorings.
+also every budget against the dense kernel: top-256 / top-512 pages on the
+29,504-token layer with both scorings, token budgets 4096 / 8192 / 16384 over
+variable chunks, and the seven ratios of the 8K-32K batched workload with
+both scorings.
 
 Prints one JSON line.  --gpus N > 1 is refused (one GPU per box).
 """
@@ -295,6 +298,88 @@ def record(name, bench, m):
         "cache_replicas": bench.replicas,
         "bytes_per_step": {"metadata": m["meta_bytes"], "selected_kv": kvb, "q_out": m["qo_bytes"]},
     }
+
+
+class ChunkedDecodeBench(DecodeBench):
+    """Decode over variable, document-aligned chunks (envelope scoring, token
+    budget): chunk scores, the longest score-order prefix that fits the budget,
+    then split-K attention over the kept chunks.  Two calls: the fused
+    selection + attention entry point takes 16-token pages only."""
+
+    def __init__(self, case, budget, dev, replicas_gib=1.0):
+        import torch
+        from block_sparse_attention_chunk_amd import ops
+        self.ops, self.torch, self.case, self.dev = ops, torch, case, dev
+        self.scoring, self.kind, self.budget = "envelope", ops.BSA_ENVELOPE, budget
+        self.which = ops.BSA_META_ENVELOPE
+        self.chunks = ops.Chunks(ops.upload(case.chunk_starts, dev), ops.upload(case.num_chunks, dev))
+        base_k, base_v = ops.upload(case.k, dev), ops.upload(case.v, dev)
+        self.q = ops.upload(case.q, dev)
+        bt, sl = ops.upload(case.block_table, dev), ops.upload(case.seq_lens, dev)
+        self.replicas = max(1, math.ceil(replicas_gib * 2 ** 30 / (case.k.nbytes + case.v.nbytes)))
+        self.reps = []
+        for r in range(self.replicas):
+            k = base_k if r == 0 else base_k.clone()
+            v = base_v if r == 0 else base_v.clone()
+            kv = ops.KVCache(k, v, sl, case.page_size, bt)
+            self.reps.append((kv, ops.build_chunk_meta(kv, self.chunks, which=self.which)))
+        kv0 = self.reps[0][0]
+        mc = self.chunks.max_chunks
+        self.max_sel = budget.max_selected(mc)
+        B, H = case.batch, case.num_kv_heads
+        self.scores = torch.empty((B, H, mc), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, H, self.max_sel), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
+        self.ws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, self.max_sel), 1),),
+                              dtype=torch.uint8, device=dev)
+        self.dws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, mc), 1),),
+                               dtype=torch.uint8, device=dev)
+        self.splits = ops.decode_num_splits(kv0, case.num_q_heads, self.max_sel)
+
+    def score(self, r):
+        kv, meta = self.reps[r]
+        self.ops.score_chunks(self.q, kv, meta, self.kind, chunks=self.chunks, out=self.scores)
+
+    def select(self, r):
+        kv, meta = self.reps[r]
+        self.ops.score_chunks(self.q, kv, meta, self.kind, chunks=self.chunks, out=self.scores)
+        self.ops.select_topk(self.scores, kv, self.budget, chunks=self.chunks, max_sel=self.max_sel,
+                             sel_idx=self.sel, sel_count=self.cnt)
+
+    def attend(self, r):
+        kv, _ = self.reps[r]
+        self.ops.sparse_attn_decode(self.q, kv, self.sel, self.cnt, chunks=self.chunks, out=self.out,
+                                    workspace=self.ws)
+
+    def dense(self, r):
+        kv, _ = self.reps[r]
+        self.ops.sparse_attn_decode(self.q, kv, None, None, chunks=self.chunks, out=self.out, workspace=self.dws)
+
+    def step(self, r):
+        self.select(r)
+        self.attend(r)
+
+    def measure(self, steps, warmup, launches=200):
+        t_step = self.time_steps(steps, warmup)
+        self.select(0)
+        self.torch.cuda.synchronize()
+        case, D, H = self.case, self.case.head_dim, self.case.num_kv_heads
+        sel, cnt = self.sel.cpu().numpy(), self.cnt.cpu().numpy()
+        kept = sum(int(case.chunk_len[b][sel[b, h, :cnt[b, h]]].sum())
+                   for b in range(case.batch) for h in range(H))
+        kv_b = kept * D * 2 * 2
+        meta_b = int(case.num_chunks.sum()) * H * 2 * D * 2
+        t_attn, t_dense = self.time_kernel(self.attend, launches), self.time_kernel(self.dense, launches)
+        return {"workload": f"variable chunks (U[16,256] tokens, {int(case.num_chunks.max())} chunks), "
+                            f"1 x {int(case.seq_lens.max())} tokens, envelope, token budget {self.budget.tokens}",
+                "budget_tokens": self.budget.tokens, "attended_tokens_per_head": kept / (case.batch * H),
+                "tokens_per_s": case.batch / t_step, "us_per_step": t_step * 1e6,
+                "score_select_us": self.time_kernel(self.select, launches) * 1e6,
+                "sparse_attn_us": t_attn * 1e6, "dense_attn_us": t_dense * 1e6,
+                "selected_kv_gbs": kv_b / t_attn / 1e9,
+                "effective_hbm_gbs": (meta_b + kv_b) / t_step / 1e9,
+                "speedup_attn_vs_dense": t_dense / t_attn, "speedup_step_vs_dense": t_dense / t_step}
 
 
 class PrefillBench:
@@ -604,6 +689,31 @@ def main():
             torch.cuda.empty_cache()
         res["layer_stack"] = stacks
     if a.extra:
+        keep = ("workload", "tokens_per_s", "us_per_step", "sparse_attn_us", "selected_kv_gbs", "selected_kv_frac",
+                "dense_attn_us", "speedup_attn_vs_dense", "speedup_step_vs_dense", "effective_hbm_gbs")
+        log("budget sweep: replay-shaped layer, 1 x 29504 tokens")
+        c1 = synth.replay_decode()
+        sweep = []
+        for scoring in ("envelope", "centroid"):
+            for k in (256, 512):
+                b1 = DecodeBench(c1, ops.Budget.topk(k), scoring, dev, a.replicas_gib)
+                rec = record(f"replay-shaped decode, 1 x 29504 tokens, {scoring}, top-{k} pages ({16 * k} tokens)",
+                             b1, b1.measure(100, 10))
+                sweep.append({k_: rec[k_] for k_ in keep})
+                del b1
+                torch.cuda.empty_cache()
+        del c1
+        res["budget_sweep"] = sweep
+        log("token-budget sweep: variable chunks, 1 x 29504 tokens")
+        c2 = synth.varchunk_decode()
+        tsa = []
+        for tokens in (4096, 8192, 16384):
+            b2 = ChunkedDecodeBench(c2, ops.Budget.token_budget(tokens), dev, a.replicas_gib)
+            tsa.append(b2.measure(100, 10))
+            del b2
+            torch.cuda.empty_cache()
+        del c2
+        res["chunk_budget_sweep"] = tsa
         log("ratio sweep: 16 sequences of 8K-32K tokens, 64 q / 8 KV heads")
         c3 = synth.batched_decode()
         sweep = []
@@ -611,10 +721,7 @@ def main():
             for ratio in synth.RATIOS:
                 b3 = DecodeBench(c3, ops.Budget.ratio_budget(ratio, bos, 1), scoring, dev, a.replicas_gib)
                 rec = record(f"batched decode, ratio {ratio}, {scoring}", b3, b3.measure(40, 5))
-                sweep.append({k: rec[k] for k in ("workload", "tokens_per_s", "us_per_step", "sparse_attn_us",
-                                                  "selected_kv_gbs", "selected_kv_frac", "dense_attn_us",
-                                                  "speedup_attn_vs_dense", "speedup_step_vs_dense",
-                                                  "effective_hbm_gbs")})
+                sweep.append({k: rec[k] for k in keep})
                 del b3
                 torch.cuda.empty_cache()
         res["ratio_sweep"] = sweep

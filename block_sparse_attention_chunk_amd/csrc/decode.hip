@@ -33,6 +33,7 @@
 // float32 caches use the same structure with 16x16x4 f32 MFMAs for S and the
 // vector ALU for P . V.
 #include "decode_common.h"
+#include "radix_select.h"
 
 namespace bsa {
 
@@ -165,6 +166,169 @@ __global__ __launch_bounds__(256) void decode_chunked_kernel(const T *__restrict
     finish_workgroup<T, D, GP>(st, regions, mbuf, lbuf, g, hq, b, h, split, splits, out, part_o, part_ml);
 }
 
+// General chunks cut into 16-token segments: variable token intervals, or
+// fixed pages of 16 tokens or more.  The workgroup first lays out the
+// segments of its row's kept chunks: each thread takes kSegItems / 256
+// consecutive chunks, and one block scan of their segment counts gives every
+// chunk its first segment number and its token range in LDS.  Segments are
+// then dealt to splits and waves round-robin like pages (segment n goes to
+// split n mod splits), so the work of a row spreads evenly whatever the chunk
+// lengths.  A wave looks up 64 of its segments at once, one per lane (binary
+// search in LDS, then the physical page of the segment's first and last token
+// from the block table: a segment of >= 16-token pages spans at most two), and
+// streams them with one segment in flight, reading the lane's values back with
+// readlane.  Rows past a segment's end are clamped onto its last row and
+// masked.
+constexpr int kSegItems = 2048;  // kept chunks per (sequence, KV head) laid out in LDS
+
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(256, 2) void decode_segments_kernel(const T *__restrict__ q, int hq, KvView kv,
+                                                                 ChunkView ch, const int32_t *__restrict__ sel_idx,
+                                                                 const int32_t *__restrict__ sel_count, int max_sel,
+                                                                 float scale_log2, int splits,
+                                                                 float *__restrict__ out, float *__restrict__ part_o,
+                                                                 float *__restrict__ part_ml) {
+    using Tr = DecTraits<T, D>;
+    constexpr int NW = Tr::kNW, VR = Tr::kVRegs, R = region_floats<D, GP>();
+    constexpr int PER = kSegItems / 256, PD = 1, NB = PD + 1;
+    __shared__ __attribute__((aligned(16))) float regions[kDecWaves * R];
+    __shared__ float mbuf[kDecWaves * 16], lbuf[kDecWaves * 16];
+    __shared__ int seg_first[kSegItems], tok_begin[kSegItems], tok_end[kSegItems];
+    __shared__ int wtot[kDecWaves];
+    args_ready(q, hq, kv.hkv, kv.seq_lens, ch.starts, ch.num, sel_idx, sel_count, max_sel, splits);
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n16 = lane & 15, G = lane >> 4;
+    const int g = hq / kv.hkv;
+    const int L = kv.seq_lens[b];
+    const int nch = ch.starts ? ch.num[b] : (L + kv.page - 1) >> kv.log2page;
+    // the kept chunks (<= kSegItems: host-checked against max_sel / max_chunks)
+    const int nitems = min(sel_idx ? sel_count[(int64_t)b * kv.hkv + h] : nch, kSegItems);
+    const int32_t *items = sel_idx ? sel_idx + ((int64_t)b * kv.hkv + h) * max_sel : nullptr;
+    const int32_t *cs = ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr;
+
+    uint4 qb[NW];
+    load_q_operand<T, D>(q, hq, g, b, h, lane, qb);
+
+    // token ranges and segment counts of this thread's chunks, then the block
+    // scan of the counts
+    int tb[PER], te[PER], before[PER], run = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = threadIdx.x * PER + k;
+        int s0 = 0, e0 = 0;
+        if (i < nitems) {
+            const int c = items ? items[i] : i;
+            if (cs) {
+                s0 = cs[c];
+                e0 = cs[c + 1];
+            } else {
+                s0 = c << kv.log2page;
+                e0 = s0 + kv.page;
+            }
+            e0 = min(e0, L);
+            s0 = min(s0, e0);
+        }
+        tb[k] = s0, te[k] = e0, before[k] = run;
+        run += (e0 - s0 + 15) >> 4;
+    }
+    const int incl = wave_scan_incl(run);
+    if (lane == 63) wtot[w] = incl;
+    __syncthreads();
+    int woff = 0, total = 0;
+#pragma unroll
+    for (int x = 0; x < kDecWaves; ++x) {
+        woff += x < w ? wtot[x] : 0;
+        total += wtot[x];
+    }
+    const int excl = woff + incl - run;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = threadIdx.x * PER + k;
+        if (i < nitems) {
+            seg_first[i] = excl + before[k];
+            tok_begin[i] = tb[k];
+            tok_end[i] = te[k];
+        }
+    }
+    __syncthreads();
+
+    WaveState<T, D, GP> st;
+    init_state(st);
+    const T *kb = reinterpret_cast<const T *>(kv.k) + (int64_t)h * kv.sh;
+    const T *vb = reinterpret_cast<const T *>(kv.v) + (int64_t)h * kv.sh;
+    const int32_t *bt = kv.bt ? kv.bt + (int64_t)b * kv.max_pages : nullptr;
+    float *region = regions + w * R;
+    const int wstride = splits * kDecWaves, first = split + splits * w;
+    const int n_mine = first < total ? (total - first + wstride - 1) / wstride : 0;
+
+    for (int base = 0; base < n_mine; base += 64) {
+        const int cnt = min(64, n_mine - base);
+        // lane l: the wave's segment base + l (clamped to the last one)
+        int my_t0, my_valid, my_p0, my_p1;
+        {
+            const int gs = first + wstride * (base + min(lane, cnt - 1));
+            int lo = 0;  // the last chunk whose first segment is <= gs
+#pragma unroll
+            for (int step = kSegItems / 2; step > 0; step >>= 1)
+                if (lo + step < nitems && seg_first[lo + step] <= gs) lo += step;
+            my_t0 = tok_begin[lo] + 16 * (gs - seg_first[lo]);
+            my_valid = min(16, tok_end[lo] - my_t0);
+            const int pa = my_t0 >> kv.log2page, pz = (my_t0 + my_valid - 1) >> kv.log2page;
+            my_p0 = bt ? bt[pa] : b * kv.max_pages + pa;
+            my_p1 = bt ? bt[pz] : b * kv.max_pages + pz;
+        }
+        auto issue = [&](int j, uint4 (&ks)[NW], uint32_t (&vr)[VR], int &valid) {
+            const int t0 = __builtin_amdgcn_readlane(my_t0, j), vl = __builtin_amdgcn_readlane(my_valid, j);
+            const int p0 = __builtin_amdgcn_readlane(my_p0, j), p1 = __builtin_amdgcn_readlane(my_p1, j);
+            const int pg0 = t0 >> kv.log2page;
+            valid = vl;
+            auto row = [&](const T *base_ptr, int slot) {
+                const int tok = t0 + min(slot, vl - 1);
+                const int phys = (tok >> kv.log2page) == pg0 ? p0 : p1;
+                return base_ptr + (int64_t)phys * kv.sp + (int64_t)(tok & (kv.page - 1)) * kv.st;
+            };
+            load_k_slice<T, D>(row(kb, n16), ks, G);
+#pragma unroll
+            for (int r = 0; r < VR / Tr::kRowRegs; ++r)
+                load_v_row<T, D>(row(vb, v_token<T, D>(r, G)), vr + r * Tr::kRowRegs, lane);
+        };
+        auto clear_tail = [&](uint32_t (&vr)[VR], int valid) {
+#pragma unroll
+            for (int r = 0; r < VR / Tr::kRowRegs; ++r)
+#pragma unroll
+                for (int c = 0; c < Tr::kRowRegs; ++c)
+                    vr[r * Tr::kRowRegs + c] = v_token<T, D>(r, G) < valid ? vr[r * Tr::kRowRegs + c] : 0u;
+        };
+        uint4 ks[NB][NW];
+        uint32_t vr[NB][VR];
+        int valid[NB];
+#pragma unroll
+        for (int s = 0; s < PD; ++s) issue(min(s, cnt - 1), ks[s], vr[s], valid[s]);
+        // whole rounds of NB segments, then the ones still in flight; no early
+        // exit inside a round, so the counter waits stay exact
+        const int full = cnt - cnt % NB;
+        for (int j = 0; j < full; j += NB) {
+#pragma unroll
+            for (int s = 0; s < NB; ++s) {
+                const int sn = (s + PD) % NB;
+                issue(min(j + s + PD, cnt - 1), ks[sn], vr[sn], valid[sn]);
+                __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of the consumption
+                clear_tail(vr[s], valid[s]);
+                consume<T, D, GP>(st, ks[s], vr[s], qb, valid[s], scale_log2, region, lane);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+            if (full + s < cnt) {
+                clear_tail(vr[s], valid[s]);
+                consume<T, D, GP>(st, ks[s], vr[s], qb, valid[s], scale_log2, region, lane);
+            }
+        }
+    }
+    finish_workgroup<T, D, GP>(st, regions, mbuf, lbuf, g, hq, b, h, split, splits, out, part_o, part_ml);
+}
+
 // Merge of the splits of one (sequence, query head):
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
 // One wave per row; lane s holds split s's (m, l) (splits <= 64) and every
@@ -225,8 +389,12 @@ static void launch_decode_t(const void *q, int hq, const KvView &kv, const Chunk
                             const int32_t *sel_count, int max_sel, float scale_log2, int splits, float *out,
                             float *part_o, float *part_ml, hipStream_t s) {
     dim3 grid(splits, kv.hkv, kv.batch), block(kDecWaves * 64);
+    const int max_items = sel_idx ? max_sel : ch.max_chunks;
     if (!ch.starts && kv.page == 16)
         hipLaunchKernelGGL((decode_paged16_kernel<T, D, GP, BSA_DECODE_PD>), grid, block, 0, s, (const T *)q, hq, kv, sel_idx,
+                           sel_count, max_sel, scale_log2, splits, out, part_o, part_ml);
+    else if (kv.page >= 16 && max_items <= kSegItems)
+        hipLaunchKernelGGL((decode_segments_kernel<T, D, GP>), grid, block, 0, s, (const T *)q, hq, kv, ch, sel_idx,
                            sel_count, max_sel, scale_log2, splits, out, part_o, part_ml);
     else
         hipLaunchKernelGGL((decode_chunked_kernel<T, D, GP>), grid, block, 0, s, (const T *)q, hq, kv, ch, sel_idx,
