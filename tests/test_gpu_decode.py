@@ -193,6 +193,30 @@ def test_page_size_32_uses_general_path(dev):
     run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.topk(6), splits=(0, 3))
 
 
+@pytest.mark.parametrize("page", [8, 32, 64])
+def test_other_page_sizes_never_read_past_a_chunk(dev, page):
+    """Fixed pages other than 16 tokens (8: the per-token kernel; 32 and 64:
+    the 16-token-segment kernel), NaN in every unused tail slot."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(41 + page, batch=3, seq_lens=[37, 300, 1001], num_q_heads=8, num_kv_heads=2,
+                             head_dim=128, page_size=page, pad_value=float("nan"), name=f"page{page}-nan")
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.topk(4), splits=(0, 1, 3))
+    assert np.all(np.isfinite(r["out"]))
+
+
+def test_long_chunk_lists_use_the_per_token_kernel(dev):
+    """More than 2048 kept chunks in a row (4-12-token chunks): the selected and
+    the dense call take the per-token kernel instead of the segment kernel."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.with_chunks(synth.replay_decode(cid=5, seq_len=20000), [synth.variable_chunks(5, 20000, 4, 12)])
+    assert int(case.num_chunks[0]) > 2048
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.token_budget(12000), band_exact_count=False,
+                        splits=(0, 5))
+    lens = case.chunk_len[0]
+    for h in range(case.num_kv_heads):
+        assert int(lens[r["sel"][0, h, :r["cnt"][0, h]]].sum()) <= 12000
+
+
 def test_deterministic_bits(dev):
     from block_sparse_attention_chunk_amd import ops
     case = synth.batched_decode(cid=14, batch=4, lo=2000, hi=5000)
