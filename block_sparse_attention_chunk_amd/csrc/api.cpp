@@ -168,6 +168,8 @@ static int check_meta_args(const bsa_kv *kv, const bsa_chunks *chunks, const bsa
     if ((which & BSA_META_ENVELOPE) && (!meta->kmin || !meta->kmax))
         return fail(BSA_ERR_INVALID_ARG, "meta->kmin / kmax is NULL");
     if ((which & BSA_META_CENTROID) && !meta->centroid) return fail(BSA_ERR_INVALID_ARG, "meta->centroid is NULL");
+    if (!aligned16(meta->kmin) || !aligned16(meta->kmax) || !aligned16(meta->centroid))
+        return fail(BSA_ERR_INVALID_ARG, "meta arrays must be 16-byte aligned");
     return BSA_OK;
 }
 
@@ -209,6 +211,8 @@ int bsa_score_chunks(const void *q, int32_t num_q_heads, int32_t num_rows, int32
         return fail(BSA_ERR_INVALID_ARG, "envelope scoring needs meta->kmin and meta->kmax");
     if (score_kind == BSA_CENTROID && !meta->centroid)
         return fail(BSA_ERR_INVALID_ARG, "centroid scoring needs meta->centroid");
+    if (!aligned16(meta->kmin) || !aligned16(meta->kmax) || !aligned16(meta->centroid))
+        return fail(BSA_ERR_INVALID_ARG, "meta arrays must be 16-byte aligned");
     if (rows_per_query < 1) return fail(BSA_ERR_INVALID_ARG, "rows_per_query must be >= 1");
     if (rows_per_query == 1) {
         if ((rc = check_heads(kv, num_q_heads, 16))) return rc;

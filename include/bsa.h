@@ -106,7 +106,8 @@ typedef struct {
 } bsa_chunks;
 
 /* Per-chunk metadata, each [batch][H_kv][max_chunks][D]: kmin / kmax in the
- * cache's element type (exact), centroid in float32.  A pointer may be NULL if
+ * cache's element type (exact), centroid in float32; each array 16-byte
+ * aligned (read and written as 16-byte vectors).  A pointer may be NULL if
  * the corresponding BSA_META_* bit / score kind is not used. */
 typedef struct {
     void *kmin;

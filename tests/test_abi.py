@@ -232,6 +232,20 @@ def test_update_meta_argument_checks():
     assert "max_touched" in (upd(0) and L.bsa_last_error().decode())
 
 
+def test_meta_arrays_must_be_16_byte_aligned():
+    L = _abi.lib()
+    kv = _kv()
+    for bad in (_abi.bsa_meta(FAKE + 2, FAKE, FAKE), _abi.bsa_meta(FAKE, FAKE + 8, FAKE),
+                _abi.bsa_meta(FAKE, FAKE, FAKE + 4)):
+        assert L.bsa_build_chunk_meta(ctypes.byref(kv), None, ctypes.byref(bad), 3, None) == _abi.BSA_ERR_INVALID_ARG
+        assert "16-byte aligned" in L.bsa_last_error().decode()
+        assert L.bsa_update_chunk_meta(ctypes.byref(kv), None, ctypes.byref(bad), 3, None, 1,
+                                       None) == _abi.BSA_ERR_INVALID_ARG
+        rc = L.bsa_score_chunks(FAKE, 8, 1, 1, ctypes.byref(kv), None, ctypes.byref(bad), _abi.BSA_ENVELOPE, 0,
+                                FAKE, None)
+        assert rc == _abi.BSA_ERR_INVALID_ARG and "16-byte aligned" in L.bsa_last_error().decode()
+
+
 def test_decode_outputs_must_be_16_byte_aligned():
     L = _abi.lib()
     kv = _kv()
