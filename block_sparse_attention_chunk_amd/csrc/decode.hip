@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void decode_segments_kernel(const T *__rest
     const int L = kv.seq_lens[b];
     const int nch = ch.starts ? ch.num[b] : (L + kv.page - 1) >> kv.log2page;
     // the kept chunks (<= kSegItems: host-checked against max_sel / max_chunks)
-    const int nitems = min(sel_idx ? sel_count[(int64_t)b * kv.hkv + h] : nch, kSegItems);
+    const int nitems = min(sel_idx ? min(sel_count[(int64_t)b * kv.hkv + h], max_sel) : nch, kSegItems);
     const int32_t *items = sel_idx ? sel_idx + ((int64_t)b * kv.hkv + h) * max_sel : nullptr;
     const int32_t *cs = ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr;
 
