@@ -204,12 +204,18 @@ def test_other_page_sizes_never_read_past_a_chunk(dev, page):
     assert np.all(np.isfinite(r["out"]))
 
 
-def test_long_chunk_lists_use_the_per_token_kernel(dev):
-    """More than 2048 kept chunks in a row (4-12-token chunks): the selected and
-    the dense call take the per-token kernel instead of the segment kernel."""
+@pytest.mark.parametrize("layout", ["2048 chunks", "over 2048 chunks"])
+def test_long_chunk_lists(dev, layout):
+    """Rows of exactly 2048 chunks of 10 tokens (the segment kernel at its
+    capacity) and of more than 2048 chunks of 4-12 tokens (the selected and the
+    dense call take the per-token kernel instead)."""
     from block_sparse_attention_chunk_amd import ops
-    case = synth.with_chunks(synth.replay_decode(cid=5, seq_len=20000), [synth.variable_chunks(5, 20000, 4, 12)])
-    assert int(case.num_chunks[0]) > 2048
+    if layout == "2048 chunks":
+        case = synth.with_chunks(synth.replay_decode(cid=6, seq_len=20480), [np.arange(0, 20481, 10)])
+        assert int(case.num_chunks[0]) == 2048
+    else:
+        case = synth.with_chunks(synth.replay_decode(cid=5, seq_len=20000), [synth.variable_chunks(5, 20000, 4, 12)])
+        assert int(case.num_chunks[0]) > 2048
     r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.token_budget(12000), band_exact_count=False,
                         splits=(0, 5))
     lens = case.chunk_len[0]
