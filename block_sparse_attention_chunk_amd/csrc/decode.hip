@@ -93,9 +93,11 @@ void decode_paged16_kernel(const T *__restrict__ q, int hq, KvView kv, const int
     finish_workgroup<T, D, GP>(st, regions, mbuf, lbuf, g, hq, b, h, split, splits, out, part_o, part_ml);
 }
 
-// General chunks: variable token intervals, or fixed pages of any power-of-two
-// size.  Each chunk is consumed in 16-token segments with per-lane addresses
-// (a segment may straddle two pages); only the segment's valid rows are read.
+// Per-token fallback for what the segment kernel below does not take: pages
+// under 16 tokens (a 16-token segment may span more than two of them) and rows
+// of more than 2048 kept chunks.  Each split takes a contiguous range of the
+// row's chunks, and a wave consumes one chunk at a time in 16-token segments
+// with a block-table lookup per lane; only the segment's valid rows are read.
 template <typename T, int D, int GP>
 __global__ __launch_bounds__(256) void decode_chunked_kernel(const T *__restrict__ q, int hq, KvView kv, ChunkView ch,
                                                              const int32_t *__restrict__ sel_idx,
