@@ -113,8 +113,15 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
     __shared__ __attribute__((aligned(1024))) char stage2[kPfStageBytes];
     __shared__ int blist[kPfMaxList];
     __shared__ int nblk_s;
-    // tiles in descending order: causal tiles with the most blocks start first
-    const int t = (gridDim.x >> 1) - 1 - (blockIdx.x >> 1), half = blockIdx.x & 1, h = blockIdx.y;
+    // Tiles in descending order: causal tiles with the most blocks start first.
+    // The two row halves of a tile copy the same blocks, so they take
+    // workgroups 8 apart: the dispatcher deals workgroups to the 8 XCDs
+    // round-robin, which puts both halves on one XCD, and the second half's
+    // copies hit that XCD's L2.  Groups of 16 workgroups hold both halves of 8
+    // consecutive tiles (the last group those of the remaining tiles).
+    const int n_tiles = gridDim.x >> 1, grp = blockIdx.x >> 4, pos = blockIdx.x & 15;
+    const int in_grp = min(8, n_tiles - 8 * grp);
+    const int t = n_tiles - 1 - (8 * grp + pos % in_grp), half = pos / in_grp, h = blockIdx.y;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n16 = lane & 15, G4 = lane >> 4;
     const int j = h * G + w;
