@@ -423,24 +423,29 @@ class PrefillBench:
     def dense(self, _=0):
         self.ops.sparse_attn_tile_prefill(self.q, self.kv, None, out=self.out, workspace=self.pws)
 
-    def timed(self, fn, reps):
+    def timed(self, fn, reps, repeats=5):
+        """Median over `repeats` runs of the average time of `reps` back-to-back
+        calls (HIP events on the current stream)."""
         torch = self.torch
         fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps
+        times = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        return sorted(times)[len(times) // 2]
 
     def measure(self, reps=5):
         t_meta = self.timed(self.build_meta, reps)
         t_score = self.timed(self.score, reps)
         t_route = self.timed(self.route, reps)
         t_attn = self.timed(self.attend, reps)
-        t_dense = self.timed(self.dense, max(1, reps // 2))
+        t_dense = self.timed(self.dense, 1, repeats=3)
         pc = self.pc
         g = pc.num_q_heads // pc.num_kv_heads
         kv_idx = self.r["kv_idx"].cpu().numpy()
