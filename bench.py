@@ -111,10 +111,15 @@ class DecodeBench:
         self.out = torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
         self.ws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, self.max_sel), 1),),
                               dtype=torch.uint8, device=dev)
-        self.dws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, kv0.max_pages), 1),),
-                               dtype=torch.uint8, device=dev)
         self.splits = ops.decode_num_splits(kv0, case.num_q_heads, self.max_sel)
-        self.dense_splits = ops.decode_num_splits(kv0, case.num_q_heads, kv0.max_pages)
+        # the dense baseline is timed at the automatic split count and at 2x and
+        # 4x of it (up to 64), and the fastest counts
+        auto = ops.decode_num_splits(kv0, case.num_q_heads, kv0.max_pages)
+        self.dense_candidates = sorted({min(64, auto * f) for f in (1, 2, 4)})
+        self.dense_splits = auto
+        self.dws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, kv0.max_pages,
+                                                               self.dense_candidates[-1]), 1),),
+                               dtype=torch.uint8, device=dev)
 
     # --- the hot path ---------------------------------------------------------------
     def score(self, r):
@@ -162,7 +167,19 @@ class DecodeBench:
 
     def dense(self, r):
         kv, _ = self.reps[r]
-        self.ops.sparse_attn_decode(self.q, kv, None, None, out=self.out, workspace=self.dws)
+        self.ops.sparse_attn_decode(self.q, kv, None, None, num_splits=self.dense_splits, out=self.out,
+                                    workspace=self.dws)
+
+    def time_dense(self, launches):
+        """The dense baseline at its fastest split count among the candidates."""
+        best = None
+        for s in self.dense_candidates:
+            self.dense_splits = s
+            t = self.time_kernel(self.dense, launches)
+            if best is None or t < best[0]:
+                best = (t, s)
+        self.dense_splits = best[1]
+        return best[0]
 
     def meta(self, r):
         kv, meta = self.reps[r]
@@ -255,7 +272,7 @@ class DecodeBench:
              "t_fused_kernel": self.time_kernel(self.fused_kernel, launches),
              "t_attn": self.time_kernel(self.attend, launches),
              "t_decode_kernel": self.time_kernel(self.decode_kernel, launches),
-             "t_dense": self.time_kernel(self.dense, launches),
+             "t_dense": self.time_dense(launches),
              "t_score": self.time_kernel(self.score, launches),
              "t_select": self.time_kernel(self.select, launches),
              "t_meta": self.time_kernel(self.meta, launches)}
@@ -295,6 +312,7 @@ def record(name, bench, m):
         "speedup_attn_vs_dense": m["t_dense"] / m["t_attn"],
         "speedup_step_vs_dense": m["t_dense"] / m["t_step"],
         "splits": bench.splits,
+        "dense_splits": bench.dense_splits,
         "cache_replicas": bench.replicas,
         "bytes_per_step": {"metadata": m["meta_bytes"], "selected_kv": kvb, "q_out": m["qo_bytes"]},
     }

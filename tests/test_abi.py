@@ -86,11 +86,15 @@ def test_decode_argument_checks():
 def test_decode_split_resolution():
     L = _abi.lib()
     kv = _kv(batch=16, num_kv_heads=8)
-    assert L.bsa_decode_num_splits(ctypes.byref(kv), 64, 256, 0) == 4        # ~512 workgroups
+    assert L.bsa_decode_num_splits(ctypes.byref(kv), 64, 256, 0) == 2        # ~192 workgroups
     assert L.bsa_decode_num_splits(ctypes.byref(kv), 64, 256, 5) == 5        # explicit
+    kv16 = _kv(batch=16, num_kv_heads=4)
+    assert L.bsa_decode_num_splits(ctypes.byref(kv16), 32, 256, 0) == 3
     kv1 = _kv(batch=1, num_kv_heads=4)
     assert L.bsa_decode_num_splits(ctypes.byref(kv1), 32, 256, 0) == 32      # capped at ~8 items per workgroup
-    assert L.bsa_decode_num_splits(ctypes.byref(kv1), 32, 1844, 0) == 64     # and at 64 splits
+    assert L.bsa_decode_num_splits(ctypes.byref(kv1), 32, 1844, 0) == 48
+    kv_many = _kv(batch=64, num_kv_heads=8)
+    assert L.bsa_decode_num_splits(ctypes.byref(kv_many), 64, 256, 0) == 1   # enough rows: one split, no merge
     assert L.bsa_decode_num_splits(ctypes.byref(kv1), 32, 3, 0) == 1
     assert L.bsa_decode_workspace_bytes(ctypes.byref(kv1), 32, 3, 0) == 0
 
