@@ -126,6 +126,50 @@ def test_router_prefill_small(dev, kind):
         f"trigger agreement with the all-oracle pipeline {agree:.3f}")
 
 
+@pytest.mark.parametrize("quantile,fixed,rho", [(0.0, None, 2), (1.0, None, 2), (0.5, None, 3), (0.25, 0.3, 2),
+                                                (0.25, None, 1)])
+def test_router_parameters(dev, quantile, fixed, rho):
+    """The router's quantile ends (0: nothing triggers, 1: everything below
+    the largest sigma_bar does), a fixed threshold instead of the quantile,
+    rho = 1 (expansion keeps k) and rho = 3, each recomputed by the oracle from
+    the GPU's own tile scores."""
+    from block_sparse_attention_chunk_amd import ops
+    k = 8
+    pc = synth.router_prefill(cid=107, T=4096, k=k, groups=8, tied_groups=(1, 3, 5, 7))
+    kv = ops.KVCache(ops.upload(pc.k, dev), ops.upload(pc.v, dev),
+                     torch.tensor([pc.T], dtype=torch.int32, device=dev), pc.block, token_major=True)
+    q = ops.upload(pc.q, dev)
+    meta = ops.build_chunk_meta(kv)
+    ts = ops.score_chunks(q, kv, meta, ops.BSA_ENVELOPE, rows_per_query=pc.tile, causal=True)
+    r = ops.select_topk_router(ts, k=k, rho=rho, quantile=quantile, fixed_threshold=fixed)
+    torch.cuda.synchronize()
+    g = {"ts": _np(ts), "kv_idx": _np(r["kv_idx"]), "sigma": _np(r["sigma"]), "sigma_bar": _np(r["sigma_bar"]),
+         "triggered": _np(r["triggered"]).astype(bool), "tau": float(_np(r["threshold"])[0])}
+    n_tiles = pc.T // pc.tile
+    nv = np.minimum(np.arange(n_tiles) + 1, g["ts"].shape[2])
+    ref = oracle.router(g["ts"].astype(np.float64), nv, k, rho, quantile_p=quantile, fixed_tau=fixed)
+    assert np.max(np.abs(g["sigma"] - ref["sigma"])) <= 1e-6
+    assert np.max(np.abs(g["sigma_bar"] - ref["sigma_bar"])) <= 1e-6
+    elig = ref["eligible"]
+    if fixed is None:
+        tau_ref = oracle.quantile(g["sigma_bar"][elig].astype(np.float64), quantile)
+    else:
+        tau_ref = fixed
+    assert abs(g["tau"] - tau_ref) <= 1e-6
+    clear = np.abs(g["sigma_bar"].astype(np.float64) - tau_ref) > 1e-6
+    assert np.array_equal(g["triggered"][clear], ref["triggered"][clear])
+    same = g["triggered"] == ref["triggered"]
+    assert np.array_equal(g["kv_idx"][same], ref["kv_idx"][same])
+    m = int(elig.sum())
+    if fixed is None and quantile == 0.0:
+        assert not g["triggered"].any()
+    if fixed is None and quantile == 1.0:
+        assert int(g["triggered"].sum()) >= m - 1 - int(np.sum(g["sigma_bar"][elig] == g["sigma_bar"][elig].max()))
+    if rho == 1:
+        assert np.all((g["kv_idx"] >= 0).sum(axis=2) == np.minimum(nv, k)[:, None])
+    log(f"router q={quantile} fixed={fixed} rho={rho}: {int(g['triggered'].sum())} of {m} eligible tiles triggered")
+
+
 def test_router_prefill_ragged(dev):
     from block_sparse_attention_chunk_amd import ops
     pc = synth.router_prefill(cid=105, T=1000, num_q_heads=14, num_kv_heads=2, k=4, groups=4, tied_groups=(2,))
