@@ -621,7 +621,7 @@ def cpu_baseline(case, k_pages, scoring, seconds):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path exists)"}))
+        print(json.dumps({"error": "bsa runs on one GPU: --gpus must be 1 (there is no multi-GPU path)"}))
         sys.exit(2)
     import torch
     from block_sparse_attention_chunk_amd import ops, synth

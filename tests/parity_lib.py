@@ -11,7 +11,7 @@ import numpy as np
 import oracle
 from block_sparse_attention_chunk_amd import synth
 
-# Tolerances (spec gates; denominators D = sum_d |term_d| of the oracle's dot product)
+# Tolerances (the parity gates; denominators D = sum_d |term_d| of the oracle's dot product)
 SCORE_REL = 1e-4          # |s_gpu - s_oracle| <= 1e-4 * D
 BAND_REL = 5e-4           # selection may differ only within +-5e-4 * D of the cut midpoint
 ATTN_ABS = {"bf16": 2e-3, "f32": 1e-5}
