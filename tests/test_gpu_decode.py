@@ -193,7 +193,7 @@ def test_page_size_32_uses_general_path(dev):
     run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.topk(6), splits=(0, 3))
 
 
-@pytest.mark.parametrize("page", [8, 32, 64])
+@pytest.mark.parametrize("page", [8, 32, 64, 256])
 def test_other_page_sizes_never_read_past_a_chunk(dev, page):
     """Fixed pages other than 16 tokens (8: the per-token kernel; 32 and 64:
     the 16-token-segment kernel), NaN in every unused tail slot."""
@@ -202,6 +202,22 @@ def test_other_page_sizes_never_read_past_a_chunk(dev, page):
                              head_dim=128, page_size=page, pad_value=float("nan"), name=f"page{page}-nan")
     r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.topk(4), splits=(0, 1, 3))
     assert np.all(np.isfinite(r["out"]))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64)])
+def test_variable_chunks_other_dtypes_and_head_dims(dev, dtype, d):
+    """The segment kernel's float32 path and its head_dim-64 operands: variable
+    chunks over a ragged batch, token budget, several split counts."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(60 + d, batch=2, seq_lens=[700, 1900], num_q_heads=8, num_kv_heads=2, head_dim=d,
+                             dtype=synth.F32 if dtype == "f32" else synth.BF16, name=f"varchunk-{dtype}-d{d}")
+    case = synth.with_chunks(case, [synth.variable_chunks(61, 700, 16, 96), synth.variable_chunks(62, 1900, 16, 96)])
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, ops.Budget.token_budget(400), band_exact_count=False,
+                        splits=(0, 1, 3))
+    lens = case.chunk_len
+    for b in range(case.batch):
+        for h in range(case.num_kv_heads):
+            assert int(lens[b][r["sel"][b, h, :r["cnt"][b, h]]].sum()) <= 400
 
 
 @pytest.mark.parametrize("layout", ["2048 chunks", "over 2048 chunks"])
