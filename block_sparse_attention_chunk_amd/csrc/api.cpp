@@ -3,6 +3,7 @@
 // HIP, so argument errors are reported without a device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -142,6 +143,26 @@ int resolve_splits(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     return s;
+}
+
+// The balanced schedule (one share of the rows' kept pages per compute unit)
+// replaces the split grid for automatic splits on batches of 16-token pages
+// when the library merges itself: at least 16 rows (batch x H_kv) and room
+// for long shares (rows x max items >= 192 x 256 pages).  It costs two
+// dependent memory round trips that the split grid does not pay (the counts
+// before the first page numbers, and before the merge's partials), about
+// 3 us measured on 16 equal rows, and saves the idle tail of unequal rows
+// (9-11 % at 16 x U[8K, 32K] tokens, ratios 1/4 to 1/2), so smaller steps keep
+// the split grid.
+bool balanced_applies(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
+    if (num_splits != 0 || !kv || kv->page_size != 16 || max_items < 1) return false;
+    const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
+    return rows >= 16 && rows <= bsa::kBalMaxRows && rows * max_items >= 192 * bsa::kBalWgs;
+}
+
+size_t balanced_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads) {
+    const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
+    return (size_t)(rows + bsa::kBalWgs) * (num_q_heads / kv->num_kv_heads) * (kv->head_dim + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -296,9 +317,11 @@ int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max
 
 size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits) {
     const int s = bsa_decode_num_splits(kv, num_q_heads, max_items, num_splits);
-    if (s <= 1 || !kv) return 0;
+    if (!kv || num_q_heads < 1 || kv->num_kv_heads < 1) return 0;
     // partial outputs and (max, sum) pairs of every split
-    return (size_t)kv->batch * num_q_heads * s * (kv->head_dim + 2) * sizeof(float);
+    size_t n = s <= 1 ? 0 : (size_t)kv->batch * num_q_heads * s * (kv->head_dim + 2) * sizeof(float);
+    if (balanced_applies(kv, max_items, num_splits)) n = std::max(n, balanced_workspace_bytes(kv, num_q_heads));
+    return n;
 }
 
 // Decode outputs and split partials are written as 16-byte vectors.
@@ -325,6 +348,14 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
         return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
     if (num_splits < 0) return fail(BSA_ERR_INVALID_ARG, "num_splits must be >= 0");
     const int items = sel_idx ? max_sel : c.max_chunks;
+    if (out && sel_idx && !chunks && balanced_applies(kv, items, num_splits)) {
+        const size_t need = balanced_workspace_bytes(kv, num_q_heads);
+        if (!workspace || workspace_bytes < need)
+            return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);
+        if ((rc = check_out_ws(out, workspace))) return rc;
+        return launched(bsa::launch_decode_balanced(q, num_q_heads, v, sel_idx, sel_count, max_sel, softmax_scale,
+                                                    out, workspace, (hipStream_t)stream));
+    }
     const int splits = resolve_splits(kv, items, num_splits);
     if (!out && splits == 1)
         return fail(BSA_ERR_INVALID_ARG, "out may be NULL only with more than one split (partials stay in the "

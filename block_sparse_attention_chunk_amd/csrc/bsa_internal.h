@@ -136,6 +136,15 @@ hipError_t launch_router(const float *ts, int32_t n_tiles, int32_t hkv, int32_t 
 hipError_t launch_decode(const void *q, int32_t hq, const KvView &kv, const ChunkView &ch, const int32_t *sel_idx,
                          const int32_t *sel_count, int32_t max_sel, float scale, int32_t splits, float *out,
                          void *ws, hipStream_t s);
+// Balanced decode schedule (decode.hip): kBalWgs workgroups share the kept
+// pages of all rows equally, at least kBalMinItems each; batch x H_kv rows up
+// to kBalMaxRows.  Workspace: (rows + kBalWgs) x group entries of (D + 2) floats.
+constexpr int kBalWgs = 256;
+constexpr int kBalMinItems = 16;
+constexpr int kBalMaxRows = 4096;
+hipError_t launch_decode_balanced(const void *q, int32_t hq, const KvView &kv, const int32_t *sel_idx,
+                                  const int32_t *sel_count, int32_t max_sel, float scale, float *out, void *ws,
+                                  hipStream_t s);
 hipError_t launch_decode_merge(int splits, const float *part_o, const float *part_ml, float *out, int hq, int batch,
                                int d, hipStream_t s);
 hipError_t launch_select_decode(const void *q, int32_t hq, const KvView &kv, const float *scores,

@@ -331,6 +331,194 @@ __global__ __launch_bounds__(256, 2) void decode_segments_kernel(const T *__rest
     finish_workgroup<T, D, GP>(st, regions, mbuf, lbuf, g, hq, b, h, split, splits, out, part_o, part_ml);
 }
 
+// Balanced schedule for batches (16-token pages, selected items).  With a
+// fixed split count per row, rows of unequal length leave the compute units
+// that hold short rows idle while the long ones finish, and one compute unit
+// streams pages at a roughly fixed rate whatever the number of its
+// workgroups, so the step lasts as long as its busiest unit.  Here the rows'
+// kept pages are laid end to end (row r = b * H_kv + h holds positions
+// [P_r, P_r + n_r)) and cut into kBalWgs equal shares of qn positions: one
+// workgroup per compute unit, each streaming the same number of pages.  A
+// share that crosses row ends yields one segment per row, each finished as a
+// partial of its own; the partial of (row r, workgroup w) is entry r + w of
+// the workspace (rows and shares both advance with position, so no two
+// segments share an entry, and the entries of one row are consecutive).
+__device__ __forceinline__ int bal_quantum(int total) {
+    return max((total + kBalWgs - 1) / kBalWgs, kBalMinItems);
+}
+
+__device__ __forceinline__ int bal_count(const int32_t *sel_count, int r, int max_sel) {
+    return min(max(sel_count[r], 0), max_sel);
+}
+
+__device__ __forceinline__ int wave_isum_all(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// One workgroup per compute unit: the register budget of one wave per SIMD.
+template <typename T, int D, int GP, int PD>
+__global__ __launch_bounds__(256, 1)
+void decode_balanced_kernel(const T *__restrict__ q, int hq, KvView kv, const int32_t *__restrict__ sel_idx,
+                            const int32_t *__restrict__ sel_count, int max_sel, float scale_log2,
+                            float *__restrict__ part_o, float *__restrict__ part_ml) {
+    constexpr int NW = DecTraits<T, D>::kNW, R = region_floats<D, GP>();
+    __shared__ __attribute__((aligned(16))) float regions[kDecWaves * R];
+    __shared__ float mbuf[kDecWaves * 16], lbuf[kDecWaves * 16];
+    __shared__ int pre[kBalMaxRows + 1];
+    __shared__ int wtot[kDecWaves];
+    args_ready(q, hq, kv.hkv, kv.bt, kv.seq_lens, kv.max_pages, sel_idx, sel_count, max_sel);
+    const int rows = kv.batch * kv.hkv;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int g = hq / kv.hkv;
+
+    // 1. pre[r] = P_r (exclusive prefix of the clamped counts), pre[rows] = T:
+    //    the counts are staged in LDS, then scanned 256 rows at a time
+#pragma unroll 4
+    for (int r = threadIdx.x; r < rows; r += kDecWaves * 64) pre[r] = bal_count(sel_count, r, max_sel);
+    __syncthreads();
+    int carry = 0;
+    for (int base = 0; base < rows; base += kDecWaves * 64) {
+        const int r = base + (int)threadIdx.x;
+        const int c = r < rows ? pre[r] : 0;
+        int inc = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            inc += lane >= o ? y : 0;
+        }
+        if (lane == 63) wtot[w] = inc;
+        __syncthreads();
+        int off = carry;
+        for (int k = 0; k < w; ++k) off += wtot[k];
+        if (r < rows) pre[r] = off + inc - c;
+        carry += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+        __syncthreads();  // wtot is rewritten by the next round
+    }
+    if (threadIdx.x == 0) pre[rows] = carry;
+    __syncthreads();
+
+    // 2. this workgroup's share and the row holding its first position
+    const int total = __builtin_amdgcn_readfirstlane(pre[rows]);
+    const int qn = bal_quantum(total);
+    const int start = (int)blockIdx.x * qn;
+    if (start >= total) return;
+    const int end = min(start + qn, total);
+    int lo = 0, hi = rows - 1;  // the last row r with P_r <= start (it holds start)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= start) lo = mid;
+        else hi = mid - 1;
+    }
+    lo = __builtin_amdgcn_readfirstlane(lo);
+
+    // 3. one segment per row met: items [a, e) of row r, wave w taking a + w + 4 j
+    for (int r = lo; r < rows; ++r) {
+        const int p0 = __builtin_amdgcn_readfirstlane(pre[r]), p1 = __builtin_amdgcn_readfirstlane(pre[r + 1]);
+        if (p0 >= end) break;
+        const int a = max(start, p0) - p0, e = min(end, p1) - p0;
+        if (e <= a) continue;  // an empty row
+        const int b = r / kv.hkv, h = r - b * kv.hkv;
+        const int32_t *items = sel_idx + (int64_t)r * max_sel;
+        const int first = a + w, n = e - a;
+        const int n_mine = n > w ? (n - w + kDecWaves - 1) / kDecWaves : 0;
+        // the first 64 page numbers, the row length and the query, waited for once
+        int spec = items[min(first + kDecWaves * lane, max_sel - 1)];
+        int len_ld = kv.seq_lens[b];
+        uint4 qb[NW];
+        load_q_operand<T, D>(q, hq, g, b, h, lane, qb);
+        asm volatile("" : "+v"(spec), "+v"(len_ld)::"memory");
+        const int L = __builtin_amdgcn_readfirstlane(len_ld);
+        WaveState<T, D, GP> st;
+        init_state(st);
+        const T *kb = reinterpret_cast<const T *>(kv.k) + (int64_t)h * kv.sh;
+        const T *vb = reinterpret_cast<const T *>(kv.v) + (int64_t)h * kv.sh;
+        const int32_t *bt = kv.bt ? kv.bt + (int64_t)b * kv.max_pages : nullptr;
+        auto page_of = [&](int base) {
+            if (base == 0) return spec;
+            return items[min(first + kDecWaves * (base + (int)(threadIdx.x & 63)), max_sel - 1)];
+        };
+        auto phys_of = [&](int, int page) { return bt ? bt[page] : b * kv.max_pages + page; };
+        stream_pages<T, D, GP, PD>(st, qb, kv, kb, vb, L, n_mine, page_of, phys_of, scale_log2, regions + w * R,
+                                   lane);
+        finish_workgroup_at<T, D, GP>(st, regions, mbuf, lbuf, g, 0, (int64_t)(r + (int)blockIdx.x) * g, 1,
+                                      nullptr, part_o, part_ml);
+        __syncthreads();  // the regions are reused by the next segment
+    }
+}
+
+// Merge of the balanced schedule's segments of one (sequence, query head):
+// the same weighted sum as decode_merge_kernel below, over the consecutive
+// entries the row's positions fall into (recomputed from the counts exactly
+// as the attention kernel cut them).  A row with no kept item has no entry
+// and gets 0/0, as the split path does.
+template <int D>
+__global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const int32_t *__restrict__ sel_count, int hkv,
+                                                                   int max_sel, const float *__restrict__ part_o,
+                                                                   const float *__restrict__ part_ml,
+                                                                   float *__restrict__ out, int hq) {
+    constexpr int VD = D / 64, SB = 8;
+    args_ready(sel_count, hkv, max_sel, part_o, part_ml, out, hq);
+    const int j = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int rows = (int)gridDim.y * hkv, g = hq / hkv;
+    const int r = b * hkv + j / g, jj = j - (j / g) * g;
+    int all = 0, before = 0, nr = 0;
+    for (int k = lane; k < rows; k += 64) {
+        const int c = bal_count(sel_count, k, max_sel);
+        all += c;
+        before += k < r ? c : 0;
+        nr += k == r ? c : 0;
+    }
+    all = wave_isum_all(all);
+    before = wave_isum_all(before);
+    nr = wave_isum_all(nr);
+    const int qn = bal_quantum(all);
+    const int w0 = before / qn;
+    const int nseg = nr > 0 ? (before + nr - 1) / qn - w0 + 1 : 0;
+    const int64_t prow0 = (int64_t)(r + w0) * g + jj;  // segment k: partial row prow0 + k g
+    float M = -INFINITY;
+    for (int k = lane; k < nseg; k += 64) M = fmaxf(M, part_ml[(prow0 + (int64_t)k * g) * 2]);
+    M = wave_max_all(M);
+    float acc[VD], lw = 0.f;
+#pragma unroll
+    for (int dd = 0; dd < VD; ++dd) acc[dd] = 0.f;
+    for (int k0 = 0; k0 < nseg; k0 += 64) {
+        const int kn = min(64, nseg - k0);
+        float2 ml = make_float2(-INFINITY, 0.f);
+        if (lane < kn) ml = *reinterpret_cast<const float2 *>(part_ml + (prow0 + (int64_t)(k0 + lane) * g) * 2);
+        const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+        lw += wave_sum_all(f * ml.y);
+        for (int i0 = 0; i0 < kn; i0 += SB) {
+            float ov[SB][VD];
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const float *p = part_o + (prow0 + (int64_t)(k0 + min(i0 + i, kn - 1)) * g) * D + VD * lane;
+                if constexpr (VD == 2) {
+                    const float2 x = *reinterpret_cast<const float2 *>(p);
+                    ov[i][0] = x.x, ov[i][1] = x.y;
+                } else {
+                    ov[i][0] = p[0];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(i0 + i, 63)));
+                const bool use = i0 + i < kn;
+#pragma unroll
+                for (int dd = 0; dd < VD; ++dd) acc[dd] = use ? fmaf(ws, ov[i][dd], acc[dd]) : acc[dd];
+            }
+        }
+    }
+    const int64_t row = (int64_t)b * hq + j;
+    const float inv = 1.0f / lw;
+    if constexpr (VD == 2) {
+        reinterpret_cast<float2 *>(out + row * D)[lane] = make_float2(acc[0] * inv, acc[1] * inv);
+    } else {
+        out[row * D + lane] = acc[0] * inv;
+    }
+}
+
 // Merge of the splits of one (sequence, query head):
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
 // One wave per row; lane s holds split s's (m, l) (splits <= 64) and every
@@ -446,6 +634,57 @@ hipError_t launch_decode(const void *q, int32_t hq, const KvView &kv, const Chun
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1 || !out) return e;  // no out: the partials are the result
     return launch_decode_merge(splits, part_o, part_ml, out, hq, kv.batch, kv.d, s);
+}
+
+template <typename T, int D, int GP>
+static void launch_balanced_t(const void *q, int hq, const KvView &kv, const int32_t *sel_idx,
+                              const int32_t *sel_count, int max_sel, float scale_log2, float *part_o, float *part_ml,
+                              hipStream_t s) {
+    hipLaunchKernelGGL((decode_balanced_kernel<T, D, GP, BSA_DECODE_PD>), dim3(kBalWgs), dim3(kDecWaves * 64), 0, s,
+                       (const T *)q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml);
+}
+
+template <typename T, int D>
+static void launch_balanced_g(const void *q, int hq, const KvView &kv, const int32_t *sel_idx,
+                              const int32_t *sel_count, int max_sel, float scale_log2, float *part_o, float *part_ml,
+                              hipStream_t s) {
+    const int g = hq / kv.hkv;
+    if (g <= 4)
+        launch_balanced_t<T, D, 4>(q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml, s);
+    else if (g <= 8)
+        launch_balanced_t<T, D, 8>(q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml, s);
+    else
+        launch_balanced_t<T, D, 16>(q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml, s);
+}
+
+hipError_t launch_decode_balanced(const void *q, int32_t hq, const KvView &kv, const int32_t *sel_idx,
+                                  const int32_t *sel_count, int32_t max_sel, float scale, float *out, void *ws,
+                                  hipStream_t s) {
+    const float scale_log2 = scale * kLog2e;
+    const int g = hq / kv.hkv;
+    float *part_o = (float *)ws;
+    float *part_ml = part_o + (size_t)(kv.batch * kv.hkv + kBalWgs) * g * kv.d;
+    if (kv.dtype == BSA_BF16) {
+        if (kv.d == 128)
+            launch_balanced_g<uint16_t, 128>(q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml, s);
+        else
+            launch_balanced_g<uint16_t, 64>(q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml, s);
+    } else {
+        if (kv.d == 128)
+            launch_balanced_g<float, 128>(q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml, s);
+        else
+            launch_balanced_g<float, 64>(q, hq, kv, sel_idx, sel_count, max_sel, scale_log2, part_o, part_ml, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid(hq, kv.batch);
+    if (kv.d == 128)
+        hipLaunchKernelGGL(decode_balanced_merge_kernel<128>, grid, dim3(64), 0, s, sel_count, kv.hkv, max_sel, part_o,
+                           part_ml, out, hq);
+    else
+        hipLaunchKernelGGL(decode_balanced_merge_kernel<64>, grid, dim3(64), 0, s, sel_count, kv.hkv, max_sel, part_o,
+                           part_ml, out, hq);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(int splits, const float *part_o, const float *part_ml, float *out, int hq, int batch,

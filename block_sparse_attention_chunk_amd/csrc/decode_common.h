@@ -250,15 +250,16 @@ __device__ __forceinline__ void init_state(WaveState<T, D, GP> &st) {
 }
 
 // Merge the 4 waves' states in LDS (each wave's output slice reuses its own
-// region, which no other wave touches) and write either the final output
-// (one split) or this split's partial (unnormalised o, max m, sum l).  NT is
+// region, which no other wave touches) and write either the final output of
+// the group's heads, rows out_row0 + j (part_o == NULL), or a partial
+// (unnormalised o, max m, sum l) to partial rows prow0 + j * pstride.  NT is
 // the workgroup size; waves from kDecWaves on hold no state and only help
 // with the merge.
 template <typename T, int D, int GP, int NT = kDecWaves * 64>
-__device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float *regions, float *mbuf, float *lbuf,
-                                                 int g, int hq, int b, int h, int split, int splits,
-                                                 float *__restrict__ out, float *__restrict__ part_o,
-                                                 float *__restrict__ part_ml) {
+__device__ __forceinline__ void finish_workgroup_at(WaveState<T, D, GP> &st, float *regions, float *mbuf,
+                                                    float *lbuf, int g, int64_t out_row0, int64_t prow0, int pstride,
+                                                    float *__restrict__ out, float *__restrict__ part_o,
+                                                    float *__restrict__ part_ml) {
     constexpr int R = region_floats<D, GP>();
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n16 = lane & 15, G = lane >> 4;
     const float l1 = sum_across_rows16(st.l_run);
@@ -311,14 +312,27 @@ __device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float 
             o.w = fmaf(f, r.w, o.w);
             l = fmaf(f, lbuf[ww * 16 + j], l);
         }
-        const int64_t row = (int64_t)b * hq + h * g + j;
-        if (splits == 1) {
+        if (!part_o) {
+            const int64_t row = out_row0 + j;
             *reinterpret_cast<float4 *>(out + row * D + d) = make_float4(o.x / l, o.y / l, o.z / l, o.w / l);
         } else {
-            *reinterpret_cast<float4 *>(part_o + (row * splits + split) * D + d) = o;
-            if (d == 0) *reinterpret_cast<float2 *>(part_ml + (row * splits + split) * 2) = make_float2(M, l);
+            const int64_t prow = prow0 + (int64_t)j * pstride;
+            *reinterpret_cast<float4 *>(part_o + prow * D + d) = o;
+            if (d == 0) *reinterpret_cast<float2 *>(part_ml + prow * 2) = make_float2(M, l);
         }
     }
+}
+
+// The split-K destination: split `split` of (sequence b, KV head h); the
+// partials are laid out [batch][H_q][splits] (part_o is NULL for one split).
+template <typename T, int D, int GP, int NT = kDecWaves * 64>
+__device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float *regions, float *mbuf, float *lbuf,
+                                                 int g, int hq, int b, int h, int split, int splits,
+                                                 float *__restrict__ out, float *__restrict__ part_o,
+                                                 float *__restrict__ part_ml) {
+    const int64_t row0 = (int64_t)b * hq + h * g;
+    finish_workgroup_at<T, D, GP, NT>(st, regions, mbuf, lbuf, g, row0, row0 * splits + split, splits, out, part_o,
+                                      part_ml);
 }
 
 template <typename T, int D>

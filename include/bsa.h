@@ -236,6 +236,14 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * share a workspace must not overlap.  sel_count entries must not exceed
  * max_sel.  With more than one split, out may be NULL: the merge is skipped
  * and the workspace holds the partials (layout at bsa_decode_merge).
+ * Balanced schedule: with num_splits == 0, out != NULL, a selection, no chunk
+ * list, 16-token pages, 16 <= batch x H_kv <= 4096 and batch x H_kv x max_sel
+ * >= 49152, the kept pages of all rows are laid end to end and cut into 256
+ * equal shares, one workgroup each, instead of a fixed split count per row
+ * (rows of unequal length then keep every compute unit busy to the end).
+ * Its partials live in the workspace in an internal layout and are merged
+ * by the library; bsa_decode_workspace_bytes(kv, H_q, max_sel, 0) covers
+ * both schedules.  The results differ from a split grid's in rounding only.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
  */
 int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits);
@@ -266,7 +274,8 @@ int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, 
  * scores [batch][H_kv][max_pages] from bsa_score_chunks.  The kept set is the
  * one bsa_select_topk returns for the same scores and budget, and out is
  * bit-identical to bsa_sparse_attn_decode on that set with the same split
- * count.  sel_idx / sel_count (both or neither) optionally receive the kept
+ * count, given explicitly (automatic splits there may take the balanced
+ * schedule).  sel_idx / sel_count (both or neither) optionally receive the kept
  * list as bsa_select_topk writes it (max_sel >= the largest possible
  * selection K).  Splits resolve as bsa_decode_num_splits(kv, H_q, K,
  * num_splits), num_splits in [0, 64], and each split keeps at most 2048

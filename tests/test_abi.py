@@ -99,6 +99,32 @@ def test_decode_split_resolution():
     assert L.bsa_decode_workspace_bytes(ctypes.byref(kv1), 32, 3, 0) == 0
 
 
+def test_balanced_schedule_workspace():
+    """Automatic splits on batches of 16-token pages with enough work take the
+    balanced schedule: 256 workgroup shares, one partial per (row, share) met,
+    (rows + 256) x group entries of (D + 2) floats."""
+    L = _abi.lib()
+    kv = _kv(batch=16, num_kv_heads=8, max_pages=2048)
+    split_bytes = 16 * 64 * 2 * 130 * 4                       # 2 automatic splits
+    bal_bytes = (128 + 256) * 8 * 130 * 4
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 946, 0) == max(split_bytes, bal_bytes)
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 946, 2) == split_bytes   # explicit: split grid
+    # 128 rows x 383 items < 192 x 256: the split grid only
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 383, 0) == split_bytes
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 384, 0) == max(split_bytes, bal_bytes)
+    # fewer than 16 rows: the split grid only
+    kv8 = _kv(batch=4, num_kv_heads=2, max_pages=4096)
+    s8 = L.bsa_decode_num_splits(ctypes.byref(kv8), 8, 4096, 0)
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv8), 8, 4096, 0) == 4 * 8 * s8 * 130 * 4
+    # other page sizes keep the split grid
+    kvp = _kv(batch=16, num_kv_heads=8, max_pages=2048, page_size=32, stride_page=2 * 32 * 128,
+              stride_head=32 * 128)
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kvp), 64, 946, 0) == split_bytes
+    # the balanced call checks its own workspace size
+    assert _decode(kv, hq=64, splits=0, max_sel=946, ws=FAKE, ws_bytes=bal_bytes - 1) == _abi.BSA_ERR_WORKSPACE
+    assert "%d bytes" % bal_bytes in L.bsa_last_error().decode()
+
+
 def _select(kv, budget, max_sel, chunks=None):
     L = _abi.lib()
     return L.bsa_select_topk(FAKE, ctypes.byref(kv), chunks, ctypes.byref(budget), FAKE, FAKE, max_sel, None)

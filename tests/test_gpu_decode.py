@@ -49,17 +49,20 @@ def run_decode_case(case, dev, kind, budget, forced=(), splits=(0,), check_dense
     outs = {s: ops.sparse_attn_decode(q, kv, sel, cnt, chunks, num_splits=s) for s in splits}
     dense = ops.sparse_attn_decode(q, kv, None, None, chunks) if check_dense else None
     # the fused selection + attention (16-token pages): same kept set, and the
-    # same output bits as the two calls at the same split count
+    # same output bits as the two calls on the same split grid (named
+    # explicitly: with automatic splits a large batch takes the balanced
+    # schedule in the two-call path)
     fused = {}
     if chunks is None and case.page_size == 16:
         for s in splits:
             fsel, fcnt = torch.full_like(sel, -7), torch.full_like(cnt, -7)
             fout = ops.select_attn_decode(q, kv, scores, budget, num_splits=s, sel_idx=fsel, sel_count=fcnt)
-            fused[s] = (fout, fsel, fcnt)
+            grid = ops.decode_num_splits(kv, case.num_q_heads, budget.max_selected(kv.max_pages), s)
+            fused[s] = (fout, fsel, fcnt, ops.sparse_attn_decode(q, kv, sel, cnt, num_splits=grid))
     torch.cuda.synchronize()
-    for s, (fout, fsel, fcnt) in fused.items():
+    for s, (fout, fsel, fcnt, sout) in fused.items():
         assert torch.equal(fsel, sel) and torch.equal(fcnt, cnt), f"fused selection differs (splits={s})"
-        assert torch.equal(fout, outs[s]), f"fused output not bit-identical (splits={s})"
+        assert torch.equal(fout, sout), f"fused output not bit-identical (splits={s})"
     kmin, kmax, cen = _np(meta.kmin), _np(meta.kmax), _np(meta.centroid)
     scores, sel, cnt = _np(scores), _np(sel), _np(cnt)
 
@@ -261,6 +264,50 @@ def test_batched_ratio_full_size(dev, ratio):
     case = synth.batched_decode()
     run_decode_case(case, dev, ops.BSA_CENTROID, ops.Budget.ratio_budget(ratio, 1, 1), forced=("bos", "eos"),
                     check_dense=ratio == 0.125)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_balanced_schedule_edges(dev, dtype, D):
+    """The balanced schedule (automatic splits, 16 rows with room for 4096
+    kept pages) on hand-made selections: one row keeping all 2048 pages of a 32K
+    sequence (its positions fall into 128 workgroup shares, so its merge takes
+    more than 64 partials), empty rows (0/0 = NaN, as in the oracle),
+    single-page rows and partial last pages.  Against the oracle; two calls
+    give the same bits."""
+    from block_sparse_attention_chunk_amd import ops
+    lens = [32768, 600, 100, 20, 5000, 16, 1, 3000]
+    counts = [[2048, 0], [38, 1], [0, 7], [2, 1], [313, 200], [1, 0], [1, 1], [188, 50]]
+    case = synth.make_decode(21, batch=8, seq_lens=lens, num_q_heads=8, num_kv_heads=2, head_dim=D,
+                             dtype=synth.BF16 if dtype == "bf16" else synth.F32, name=f"balanced-edges-{dtype}-{D}")
+    max_sel = 4096
+    gen = np.random.default_rng(2101)
+    sel = np.full((8, 2, max_sel), -1, dtype=np.int32)
+    cnt = np.array(counts, dtype=np.int32)
+    for b in range(8):
+        pages = (lens[b] + 15) // 16
+        for h in range(2):
+            sel[b, h, :cnt[b, h]] = np.sort(gen.choice(pages, size=cnt[b, h], replace=False))
+    log(f"case {case.name}: counts {counts}")
+    kv, _ = gpu_kv(case, dev)
+    q = ops.upload(case.q, dev)
+    sel_t, cnt_t = ops.upload(sel, dev), ops.upload(cnt, dev)
+    # the automatic call takes the balanced schedule: a workspace sized for the
+    # split grid alone is refused
+    grid = ops.decode_num_splits(kv, 8, max_sel)
+    small = torch.zeros((8 * 8 * grid * (D + 2) * 4,), dtype=torch.uint8, device=dev)
+    assert ops.decode_workspace_bytes(kv, 8, max_sel) == (16 + 256) * 4 * (D + 2) * 4 > small.numel()
+    with pytest.raises(RuntimeError, match="workspace"):
+        ops.sparse_attn_decode(q, kv, sel_t, cnt_t, workspace=small)
+    out1 = _np(ops.sparse_attn_decode(q, kv, sel_t, cnt_t))
+    out2 = _np(ops.sparse_attn_decode(q, kv, sel_t, cnt_t))
+    assert np.array_equal(out1, out2, equal_nan=True)
+    ref = oracle.decode_attn(case.q, oracle_cache(case), sel, cnt)
+    g = 4
+    empty = np.repeat(cnt == 0, g, axis=1)                     # [B][H_q]
+    assert np.all(np.isnan(out1[empty])) and np.all(np.isnan(ref[empty]))
+    err = max_abs(out1[~empty], ref[~empty])
+    log(f"  ok: attn err {err:.2e}")
+    assert err <= ATTN_ABS[dtype]
 
 
 def test_partials_then_merge_matches_one_call(dev):
