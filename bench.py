@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the router prefill records")
     ap.add_argument("--no-layers", action="store_true", help="skip the 48-layer decode-step records")
     ap.add_argument("--extra", action="store_true", help="also the seven-ratio batched sweep")
+    ap.add_argument("--extra-ratios", type=str, default="",
+                    help="comma-separated subset of the sweep's ratios (default: all seven)")
     ap.add_argument("--only-headline-kernel", action="store_true",
                     help="profiling aid: time only the headline workload")
     ap.add_argument("--kernel-launches", type=int, default=200, help="launches per per-kernel timing loop")
@@ -301,6 +303,8 @@ def record(name, bench, m):
         "fused_kernel_us": m["t_fused_kernel"] * 1e6,
         "fused_kernel_selected_kv_gbs": kvb / m["t_fused_kernel"] / 1e9,
         "sparse_attn_us": m["t_attn"] * 1e6,
+        # selected K/V over the whole attention call (automatic schedule, merge included)
+        "attn_selected_kv_gbs": kvb / m["t_attn"] / 1e9,
         "decode_kernel_us": m["t_decode_kernel"] * 1e6,
         "merge_kernel_us": m["t_merge"] * 1e6,
         "selected_kv_gbs": kvb / m["t_decode_kernel"] / 1e9,
@@ -712,7 +716,8 @@ def main():
             torch.cuda.empty_cache()
         res["layer_stack"] = stacks
     if a.extra:
-        keep = ("workload", "tokens_per_s", "us_per_step", "sparse_attn_us", "selected_kv_gbs", "selected_kv_frac",
+        keep = ("workload", "tokens_per_s", "us_per_step", "unfused_us_per_step", "sparse_attn_us", "attn_selected_kv_gbs",
+                "selected_kv_gbs", "selected_kv_frac",
                 "dense_attn_us", "speedup_attn_vs_dense", "speedup_step_vs_dense", "effective_hbm_gbs")
         log("budget sweep: replay-shaped layer, 1 x 29504 tokens")
         c1 = synth.replay_decode()
@@ -740,8 +745,9 @@ def main():
         log("ratio sweep: 16 sequences of 8K-32K tokens, 64 q / 8 KV heads")
         c3 = synth.batched_decode()
         sweep = []
+        ratios = [float(x) for x in a.extra_ratios.split(",")] if a.extra_ratios else synth.RATIOS
         for scoring, bos in (("centroid", 1), ("envelope", 0)):
-            for ratio in synth.RATIOS:
+            for ratio in ratios:
                 b3 = DecodeBench(c3, ops.Budget.ratio_budget(ratio, bos, 1), scoring, dev, a.replicas_gib)
                 rec = record(f"batched decode, ratio {ratio}, {scoring}", b3, b3.measure(40, 5))
                 sweep.append({k: rec[k] for k in keep})
