@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 from block_sparse_attention_chunk_amd import synth
-from parity_lib import (ATTN_ABS, check_band, check_scores, gpu_kv, log, max_abs, oracle_cache, oracle_select)
+from parity_lib import (ATTN_ABS, check_band, check_scores, gpu_kv, log, max_abs, oracle_cache, oracle_select,
+                        unequal_rows_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -275,19 +276,9 @@ def test_balanced_schedule_edges(dev, dtype, D):
     single-page rows and partial last pages.  Against the oracle; two calls
     give the same bits."""
     from block_sparse_attention_chunk_amd import ops
-    lens = [32768, 600, 100, 20, 5000, 16, 1, 3000]
-    counts = [[2048, 0], [38, 1], [0, 7], [2, 1], [313, 200], [1, 0], [1, 1], [188, 50]]
-    case = synth.make_decode(21, batch=8, seq_lens=lens, num_q_heads=8, num_kv_heads=2, head_dim=D,
-                             dtype=synth.BF16 if dtype == "bf16" else synth.F32, name=f"balanced-edges-{dtype}-{D}")
-    max_sel = 4096
-    gen = np.random.default_rng(2101)
-    sel = np.full((8, 2, max_sel), -1, dtype=np.int32)
-    cnt = np.array(counts, dtype=np.int32)
-    for b in range(8):
-        pages = (lens[b] + 15) // 16
-        for h in range(2):
-            sel[b, h, :cnt[b, h]] = np.sort(gen.choice(pages, size=cnt[b, h], replace=False))
-    log(f"case {case.name}: counts {counts}")
+    case, sel, cnt = unequal_rows_case(21, synth.BF16 if dtype == "bf16" else synth.F32, D, 2101)
+    max_sel = sel.shape[2]
+    log(f"case {case.name}: counts {cnt.tolist()}")
     kv, _ = gpu_kv(case, dev)
     q = ops.upload(case.q, dev)
     sel_t, cnt_t = ops.upload(sel, dev), ops.upload(cnt, dev)

@@ -2,9 +2,9 @@
 stream it is given (here torch's current stream), so the path runs on a side
 stream and inside a captured HIP graph.
 
-A graph of the decode step (scores, fused selection + attention, merge) and
-one of the router prefill (tile scores, router, tile attention) are each
-replayed three times, with unrelated eager work on the same buffers and a
+A graph of the decode step (scores, fused selection + attention, merge), one
+of the balanced decode schedule and one of the router prefill (tile scores,
+router, tile attention) are each replayed three times, with unrelated eager work on the same buffers and a
 synchronisation between replays; every replay must give the eager result bit
 for bit.  The library records no memset and allocates nothing, so a replay
 redoes exactly the eager work.
@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from block_sparse_attention_chunk_amd import synth
-from parity_lib import gpu_kv, log
+from parity_lib import gpu_kv, log, unequal_rows_case
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,42 @@ def test_decode_graph_replays_match_eager(dev):
         torch.cuda.synchronize()
         log(f"decode graph replay {rep}")
         assert torch.equal(out, ref), f"replay {rep} differs from the eager result"
+
+
+def test_balanced_decode_graph_replays_match_eager(dev):
+    """The balanced decode schedule (16 rows of very unequal length,
+    automatic splits) captured and replayed; between replays the workspace is
+    cleared, so a replay must not depend on what an earlier call left there."""
+    from block_sparse_attention_chunk_amd import ops
+    case, sel, cnt = unequal_rows_case(22, synth.BF16, 128, 2201)
+    kv, _ = gpu_kv(case, dev)
+    q, sel_t, cnt_t = ops.upload(case.q, dev), ops.upload(sel, dev), ops.upload(cnt, dev)
+    ws = torch.zeros((ops.decode_workspace_bytes(kv, 8, sel.shape[2]),), dtype=torch.uint8, device=dev)
+    out = torch.empty((8, 8, 128), dtype=torch.float32, device=dev)
+
+    def attend():
+        ops.sparse_attn_decode(q, kv, sel_t, cnt_t, out=out, workspace=ws)
+
+    attend()
+    torch.cuda.synchronize()
+    ref = out.cpu().numpy()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        attend()
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        attend()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"balanced decode graph replay {rep}")
+        assert np.array_equal(out.cpu().numpy(), ref, equal_nan=True), f"replay {rep} differs from the eager result"
 
 
 def test_router_prefill_graph_replays_match_eager(dev):
