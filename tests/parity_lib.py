@@ -17,15 +17,15 @@ BAND_REL = 5e-4           # selection may differ only within +-5e-4 * D of the c
 ATTN_ABS = {"bf16": 2e-3, "f32": 1e-5}
 
 
-def unequal_rows_case(cid: int, dtype: str, head_dim: int, sel_seed: int):
-    """8 sequences x 2 KV heads (8 q heads) with hand-made selections of very
+def unequal_rows_case(cid: int, dtype: str, head_dim: int, sel_seed: int, num_q_heads: int = 8):
+    """8 sequences x 2 KV heads (num_q_heads q heads) with hand-made selections of very
     unequal sizes, in a kept-list capacity of 4096 pages: one row keeps all
     2048 pages of a 32K sequence, two rows keep nothing, several keep one page,
     and partial last pages occur.  Returns (case, sel_idx, sel_count)."""
     lens = [32768, 600, 100, 20, 5000, 16, 1, 3000]
     counts = [[2048, 0], [38, 1], [0, 7], [2, 1], [313, 200], [1, 0], [1, 1], [188, 50]]
-    case = synth.make_decode(cid, batch=8, seq_lens=lens, num_q_heads=8, num_kv_heads=2, head_dim=head_dim,
-                             dtype=dtype, name=f"unequal-rows-{dtype}-{head_dim}")
+    case = synth.make_decode(cid, batch=8, seq_lens=lens, num_q_heads=num_q_heads, num_kv_heads=2,
+                             head_dim=head_dim, dtype=dtype, name=f"unequal-rows-{dtype}-{head_dim}-{num_q_heads}q")
     gen = np.random.default_rng(sel_seed)
     sel = np.full((8, 2, 4096), -1, dtype=np.int32)
     cnt = np.array(counts, dtype=np.int32)

@@ -267,16 +267,16 @@ def test_batched_ratio_full_size(dev, ratio):
                     check_dense=ratio == 0.125)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
-def test_balanced_schedule_edges(dev, dtype, D):
+@pytest.mark.parametrize("dtype,D,hq", [("bf16", 128, 8), ("f32", 64, 8), ("bf16", 64, 32), ("f32", 128, 32)])
+def test_balanced_schedule_edges(dev, dtype, D, hq):
     """The balanced schedule (automatic splits, 16 rows with room for 4096
     kept pages) on hand-made selections: one row keeping all 2048 pages of a 32K
     sequence (its positions fall into 128 workgroup shares, so its merge takes
     more than 64 partials), empty rows (0/0 = NaN, as in the oracle),
-    single-page rows and partial last pages.  Against the oracle; two calls
-    give the same bits."""
+    single-page rows and partial last pages; query groups of 4 and 16 heads.
+    Against the oracle; two calls give the same bits."""
     from block_sparse_attention_chunk_amd import ops
-    case, sel, cnt = unequal_rows_case(21, synth.BF16 if dtype == "bf16" else synth.F32, D, 2101)
+    case, sel, cnt = unequal_rows_case(21, synth.BF16 if dtype == "bf16" else synth.F32, D, 2101, hq)
     max_sel = sel.shape[2]
     log(f"case {case.name}: counts {cnt.tolist()}")
     kv, _ = gpu_kv(case, dev)
@@ -284,16 +284,16 @@ def test_balanced_schedule_edges(dev, dtype, D):
     sel_t, cnt_t = ops.upload(sel, dev), ops.upload(cnt, dev)
     # the automatic call takes the balanced schedule: a workspace sized for the
     # split grid alone is refused
-    grid = ops.decode_num_splits(kv, 8, max_sel)
-    small = torch.zeros((8 * 8 * grid * (D + 2) * 4,), dtype=torch.uint8, device=dev)
-    assert ops.decode_workspace_bytes(kv, 8, max_sel) == (16 + 256) * 4 * (D + 2) * 4 > small.numel()
+    g = hq // 2
+    grid = ops.decode_num_splits(kv, hq, max_sel)
+    small = torch.zeros((8 * hq * grid * (D + 2) * 4,), dtype=torch.uint8, device=dev)
+    assert ops.decode_workspace_bytes(kv, hq, max_sel) == (16 + 256) * g * (D + 2) * 4 > small.numel()
     with pytest.raises(RuntimeError, match="workspace"):
         ops.sparse_attn_decode(q, kv, sel_t, cnt_t, workspace=small)
     out1 = _np(ops.sparse_attn_decode(q, kv, sel_t, cnt_t))
     out2 = _np(ops.sparse_attn_decode(q, kv, sel_t, cnt_t))
     assert np.array_equal(out1, out2, equal_nan=True)
     ref = oracle.decode_attn(case.q, oracle_cache(case), sel, cnt)
-    g = 4
     empty = np.repeat(cnt == 0, g, axis=1)                     # [B][H_q]
     assert np.all(np.isnan(out1[empty])) and np.all(np.isnan(ref[empty]))
     err = max_abs(out1[~empty], ref[~empty])
