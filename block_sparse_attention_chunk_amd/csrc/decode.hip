@@ -31,7 +31,9 @@
 // make the partials of all XCDs visible).  HBM-bound.
 //
 // float32 caches use the same structure with 16x16x4 f32 MFMAs for S and the
-// vector ALU for P . V.
+// vector ALU for P . V.  Large batches of 16-token pages can instead take the
+// balanced schedule further down (equal shares of all rows' pages, one
+// workgroup per compute unit), with the same per-page machinery.
 #include "decode_common.h"
 #include "radix_select.h"
 
