@@ -171,8 +171,8 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(const uint16_t *
             qv[s] = *reinterpret_cast<const uint4 *>(q + ((int64_t)b * hq + h * g + jq) * D + 32 * s + 8 * G);
     }
     // rows are clamped into the allocated max_chunks, not to the row length, so
-    // the first requests do not wait for it; rows past the length are scored
-    // and discarded
+    // the first requests do not wait for it; chunks past the length within the
+    // last live group are scored and discarded
     auto load = [&](int grp, uint4 (&a)[NS]) {
         const int c = min(grp * 16 + n16, ch.max_chunks - 1);
         const int64_t mrow = mbase + (int64_t)c * D;
@@ -270,12 +270,23 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(const uint16_t *
             }
         }
     };
-    for (int grp = first; grp < n_groups; grp += 2 * stride) {
-        load(min(grp + stride, n_groups - 1), aB);   // unconditional: exact memory counters
+    // only the groups holding the row's chunks are read; the slots past them
+    // (up to max_chunks) get -inf without a load
+    const int n_live = min((n + 15) >> 4, n_groups);
+    int grp = first;
+    for (; grp < n_live; grp += 2 * stride) {
+        load(min(grp + stride, n_live - 1), aB);   // unconditional: exact memory counters
         score(grp, aA);
-        if (grp + stride >= n_groups) break;
-        load(min(grp + 2 * stride, n_groups - 1), aA);
+        if (grp + stride >= n_live) {
+            grp += stride;
+            break;
+        }
+        load(min(grp + 2 * stride, n_live - 1), aA);
         score(grp + stride, aB);
+    }
+    for (; grp < n_groups; grp += stride) {
+        const int cc = grp * 16 + lane;
+        if (lane < 16 && cc < ch.max_chunks) orow[cc] = -INFINITY;
     }
 }
 
