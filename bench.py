@@ -685,6 +685,14 @@ def main():
                             "bos+eos (4096 tokens per sequence and head)", b3, b3.measure(max(50, a.steps // 4), 5)))
         del b3, c3
         torch.cuda.empty_cache()
+        log("batched: 64 q / 8 KV heads, 16 x U[8K, 32K] tokens, ratio 1/2")
+        cr = synth.batched_decode()
+        br = DecodeBench(cr, ops.Budget.ratio_budget(0.5, 1, 1), "centroid", dev, a.replicas_gib)
+        extra.append(record("batched decode, 64 q / 8 KV heads, 16 x U[8192, 32768] tokens (8,409-30,271), centroid, "
+                            "ratio 1/2 with bos+eos; attention call on the balanced schedule", br,
+                            br.measure(max(50, a.steps // 4), 5)))
+        del br, cr
+        torch.cuda.empty_cache()
         res["batched"] = extra
     if not a.no_prefill and not a.only_headline_kernel:
         log("router prefill: 131072 tokens")
