@@ -301,6 +301,37 @@ def test_balanced_schedule_edges(dev, dtype, D, hq):
     assert err <= ATTN_ABS[dtype]
 
 
+def test_balanced_schedule_4096_rows(dev):
+    """The balanced schedule at its row limit: 512 sequences x 8 KV heads =
+    4096 rows (the counts' prefix is built in 16 rounds of 256 rows), lengths
+    U[1, 256] tokens, random kept sets of 0-16 pages per row; against the
+    oracle.  One row more and the call keeps the split grid."""
+    from block_sparse_attention_chunk_amd import ops
+    gen = np.random.default_rng(2301)
+    B, H, D = 512, 8, 64
+    lens = gen.integers(1, 257, size=B)
+    case = synth.make_decode(23, batch=B, seq_lens=lens, num_q_heads=H, num_kv_heads=H, head_dim=D,
+                             dtype=synth.BF16, name="balanced-4096-rows")
+    max_sel = 16
+    sel = np.full((B, H, max_sel), -1, dtype=np.int32)
+    cnt = np.zeros((B, H), dtype=np.int32)
+    for b in range(B):
+        pages = (int(lens[b]) + 15) // 16
+        for h in range(H):
+            c = int(gen.integers(0, pages + 1))
+            cnt[b, h] = c
+            sel[b, h, :c] = np.sort(gen.choice(pages, size=c, replace=False))
+    kv, _ = gpu_kv(case, dev)
+    assert ops.decode_workspace_bytes(kv, H, max_sel) == (4096 + 256) * 1 * (D + 2) * 4
+    out = _np(ops.sparse_attn_decode(ops.upload(case.q, dev), kv, ops.upload(sel, dev), ops.upload(cnt, dev)))
+    ref = oracle.decode_attn(case.q, oracle_cache(case), sel, cnt)
+    empty = cnt == 0
+    assert np.all(np.isnan(out[empty])) and np.all(np.isnan(ref[empty]))
+    err = max_abs(out[~empty], ref[~empty])
+    log(f"  4096 rows: {int(empty.sum())} empty, attn err {err:.2e}")
+    assert err <= ATTN_ABS["bf16"]
+
+
 def test_partials_then_merge_matches_one_call(dev):
     """out == NULL leaves the split partials in the workspace; bsa_decode_merge
     on them gives the same bits as the single call (unfused and fused)."""
