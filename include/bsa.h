@@ -231,8 +231,9 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * q [batch][H_q][D] (kv dtype); out [batch][H_q][D] float32; q, out and
  * workspace 16-byte aligned.
  * Group size H_q/H_kv <= 16.  workspace >= bsa_decode_workspace_bytes(...)
- * (0 bytes when the resolved split count is 1): the split partials, merged
- * by a second kernel on the same stream.  Splits are capped at 64.  Calls that
+ * (0 bytes when the resolved split count is 1 and the balanced schedule below
+ * does not apply): the partials, merged by a second kernel on the same
+ * stream.  Splits are capped at 64.  Calls that
  * share a workspace must not overlap.  sel_count entries must not exceed
  * max_sel.  With more than one split, out may be NULL: the merge is skipped
  * and the workspace holds the partials (layout at bsa_decode_merge).
