@@ -162,7 +162,15 @@ bool balanced_applies(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
 
 size_t balanced_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads) {
     const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
-    return (size_t)(rows + bsa::kBalWgs) * (num_q_heads / kv->num_kv_heads) * (kv->head_dim + 2) * sizeof(float);
+    const size_t n = (size_t)(rows + bsa::kBalWgs) * (num_q_heads / kv->num_kv_heads) * (kv->head_dim + 2) * sizeof(float);
+    return (n + 15) & ~(size_t)15;
+}
+
+// The fused entry point on the balanced schedule keeps the kept lists (max
+// items and a count per row) after the partials when the caller takes none.
+size_t balanced_list_bytes(const bsa_kv *kv, int32_t max_items) {
+    const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
+    return (size_t)rows * (max_items + 1) * sizeof(int32_t);
 }
 
 }  // namespace
@@ -320,7 +328,8 @@ size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t
     if (!kv || num_q_heads < 1 || kv->num_kv_heads < 1) return 0;
     // partial outputs and (max, sum) pairs of every split
     size_t n = s <= 1 ? 0 : (size_t)kv->batch * num_q_heads * s * (kv->head_dim + 2) * sizeof(float);
-    if (balanced_applies(kv, max_items, num_splits)) n = std::max(n, balanced_workspace_bytes(kv, num_q_heads));
+    if (balanced_applies(kv, max_items, num_splits))
+        n = std::max(n, balanced_workspace_bytes(kv, num_q_heads) + balanced_list_bytes(kv, max_items));
     return n;
 }
 
@@ -391,6 +400,30 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
     if (sel_idx && max_sel < need)
         return fail(BSA_ERR_INVALID_ARG, "max_sel %d is smaller than the largest possible selection %lld", max_sel,
                     (long long)need);
+    if (out && balanced_applies(kv, (int)need, num_splits)) {
+        // a large batch: the selection kernel, then the attention on the
+        // balanced schedule (the same kernels and bits as the two calls)
+        const size_t part = balanced_workspace_bytes(kv, num_q_heads);
+        const size_t ws_need = part + (sel_idx ? 0 : balanced_list_bytes(kv, (int)need));
+        if (!workspace || workspace_bytes < ws_need)
+            return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", ws_need, workspace_bytes);
+        if ((rc = check_out_ws(out, workspace))) return rc;
+        const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
+        int32_t *si = sel_idx, *sc = sel_count;
+        int32_t ms = max_sel;
+        if (!si) {
+            si = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + part);
+            sc = si + rows * need;
+            ms = (int32_t)need;
+        }
+        bsa::ChunkView c;
+        check_chunks(kv, nullptr, &c);
+        hipError_t e = bsa::launch_select(scores, v, c, *budget, si, sc, ms, (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = bsa::launch_decode_balanced(q, num_q_heads, v, si, sc, ms, softmax_scale, out, workspace,
+                                            (hipStream_t)stream);
+        return launched(e);
+    }
     const int splits = resolve_splits(kv, (int)need, num_splits);
     if ((need + splits - 1) / splits > kMaxItemsPerSplit)
         return fail(BSA_ERR_INVALID_ARG, "%d splits keep more than %d pages each; use more splits", splits,

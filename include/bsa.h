@@ -244,7 +244,8 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * (rows of unequal length then keep every compute unit busy to the end).
  * Its partials live in the workspace in an internal layout and are merged
  * by the library; bsa_decode_workspace_bytes(kv, H_q, max_sel, 0) covers
- * both schedules.  The results differ from a split grid's in rounding only.
+ * both schedules (and the kept lists bsa_select_attn_decode may keep there).
+ * The results differ from a split grid's in rounding only.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
  */
 int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits);
@@ -275,8 +276,12 @@ int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, 
  * scores [batch][H_kv][max_pages] from bsa_score_chunks.  The kept set is the
  * one bsa_select_topk returns for the same scores and budget, and out is
  * bit-identical to bsa_sparse_attn_decode on that set with the same split
- * count, given explicitly (automatic splits there may take the balanced
- * schedule).  sel_idx / sel_count (both or neither) optionally receive the kept
+ * count (for num_splits = 0, with max_sel equal to the largest possible
+ * selection K there).  With num_splits = 0 and out given on a batch where the
+ * balanced schedule applies (see bsa_sparse_attn_decode, with K for max_sel),
+ * this call runs the selection kernel of bsa_select_topk and then the
+ * balanced attention instead of the fused kernel; the kept lists then stay in
+ * the workspace unless sel_idx is given.  sel_idx / sel_count (both or neither) optionally receive the kept
  * list as bsa_select_topk writes it (max_sel >= the largest possible
  * selection K).  Splits resolve as bsa_decode_num_splits(kv, H_q, K,
  * num_splits), num_splits in [0, 64], and each split keeps at most 2048

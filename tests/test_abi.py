@@ -107,11 +107,12 @@ def test_balanced_schedule_workspace():
     kv = _kv(batch=16, num_kv_heads=8, max_pages=2048)
     split_bytes = 16 * 64 * 2 * 130 * 4                       # 2 automatic splits
     bal_bytes = (128 + 256) * 8 * 130 * 4
-    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 946, 0) == max(split_bytes, bal_bytes)
+    lists = 128 * (946 + 1) * 4                               # kept lists of the fused entry point
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 946, 0) == max(split_bytes, bal_bytes + lists)
     assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 946, 2) == split_bytes   # explicit: split grid
     # 128 rows x 383 items < 192 x 256: the split grid only
     assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 383, 0) == split_bytes
-    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 384, 0) == max(split_bytes, bal_bytes)
+    assert L.bsa_decode_workspace_bytes(ctypes.byref(kv), 64, 384, 0) == max(split_bytes, bal_bytes + 128 * 385 * 4)
     # fewer than 16 rows: the split grid only
     kv8 = _kv(batch=4, num_kv_heads=2, max_pages=4096)
     s8 = L.bsa_decode_num_splits(ctypes.byref(kv8), 8, 4096, 0)

@@ -50,20 +50,22 @@ def run_decode_case(case, dev, kind, budget, forced=(), splits=(0,), check_dense
     outs = {s: ops.sparse_attn_decode(q, kv, sel, cnt, chunks, num_splits=s) for s in splits}
     dense = ops.sparse_attn_decode(q, kv, None, None, chunks) if check_dense else None
     # the fused selection + attention (16-token pages): same kept set, and the
-    # same output bits as the two calls on the same split grid (named
-    # explicitly: with automatic splits a large batch takes the balanced
-    # schedule in the two-call path)
+    # same output bits as the two calls with the same num_splits (with 0 on a
+    # large batch both take the balanced schedule), and, with the split grid
+    # named explicitly, as the two calls on that grid
     fused = {}
     if chunks is None and case.page_size == 16:
         for s in splits:
             fsel, fcnt = torch.full_like(sel, -7), torch.full_like(cnt, -7)
             fout = ops.select_attn_decode(q, kv, scores, budget, num_splits=s, sel_idx=fsel, sel_count=fcnt)
             grid = ops.decode_num_splits(kv, case.num_q_heads, budget.max_selected(kv.max_pages), s)
-            fused[s] = (fout, fsel, fcnt, ops.sparse_attn_decode(q, kv, sel, cnt, num_splits=grid))
+            gout = ops.select_attn_decode(q, kv, scores, budget, num_splits=grid)
+            fused[s] = (fout, fsel, fcnt, gout, ops.sparse_attn_decode(q, kv, sel, cnt, num_splits=grid))
     torch.cuda.synchronize()
-    for s, (fout, fsel, fcnt, sout) in fused.items():
+    for s, (fout, fsel, fcnt, gout, sout) in fused.items():
         assert torch.equal(fsel, sel) and torch.equal(fcnt, cnt), f"fused selection differs (splits={s})"
-        assert torch.equal(fout, sout), f"fused output not bit-identical (splits={s})"
+        assert torch.equal(fout, outs[s]), f"fused output not bit-identical (splits={s})"
+        assert torch.equal(gout, sout), f"fused output not bit-identical on the split grid (splits={s})"
     kmin, kmax, cen = _np(meta.kmin), _np(meta.kmax), _np(meta.centroid)
     scores, sel, cnt = _np(scores), _np(sel), _np(cnt)
 
@@ -287,7 +289,8 @@ def test_balanced_schedule_edges(dev, dtype, D, hq):
     g = hq // 2
     grid = ops.decode_num_splits(kv, hq, max_sel)
     small = torch.zeros((8 * hq * grid * (D + 2) * 4,), dtype=torch.uint8, device=dev)
-    assert ops.decode_workspace_bytes(kv, hq, max_sel) == (16 + 256) * g * (D + 2) * 4 > small.numel()
+    assert ops.decode_workspace_bytes(kv, hq, max_sel) == (16 + 256) * g * (D + 2) * 4 + 16 * (max_sel + 1) * 4
+    assert (16 + 256) * g * (D + 2) * 4 > small.numel()
     with pytest.raises(RuntimeError, match="workspace"):
         ops.sparse_attn_decode(q, kv, sel_t, cnt_t, workspace=small)
     out1 = _np(ops.sparse_attn_decode(q, kv, sel_t, cnt_t))
@@ -322,7 +325,7 @@ def test_balanced_schedule_4096_rows(dev):
             cnt[b, h] = c
             sel[b, h, :c] = np.sort(gen.choice(pages, size=c, replace=False))
     kv, _ = gpu_kv(case, dev)
-    assert ops.decode_workspace_bytes(kv, H, max_sel) == (4096 + 256) * 1 * (D + 2) * 4
+    assert ops.decode_workspace_bytes(kv, H, max_sel) == (4096 + 256) * 1 * (D + 2) * 4 + 4096 * (max_sel + 1) * 4
     out = _np(ops.sparse_attn_decode(ops.upload(case.q, dev), kv, ops.upload(sel, dev), ops.upload(cnt, dev)))
     ref = oracle.decode_attn(case.q, oracle_cache(case), sel, cnt)
     empty = cnt == 0
