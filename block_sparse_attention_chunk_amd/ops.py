@@ -274,7 +274,9 @@ def sparse_attn_decode(q: torch.Tensor, kv: KVCache, sel_idx: Optional[torch.Ten
                        scale: Optional[float] = None, num_splits: int = 0, out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bsa_sparse_attn_decode: q [B][H_q][D] -> out [B][H_q][D] float32; sel_idx None = dense.
-    out=PARTIALS leaves the split partials in the workspace (see decode_merge)."""
+    out=PARTIALS leaves the split partials in the workspace (see decode_merge).
+    With automatic splits (num_splits=0), out given and a large batch of
+    16-token pages, the attention runs on the balanced schedule."""
     B, Hq, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -316,7 +318,9 @@ def select_attn_decode(q: torch.Tensor, kv: KVCache, scores: torch.Tensor, budge
                        sel_count: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bsa_select_attn_decode: selection + attention in one launch (16-token
     pages).  q [B][H_q][D], scores [B][H_kv][max_pages] -> out [B][H_q][D]
-    float32; sel_idx / sel_count, when given, receive the kept list."""
+    float32; sel_idx / sel_count, when given, receive the kept list.  With
+    automatic splits on a large batch the library runs the selection kernel
+    and the balanced attention instead (the same bits as the two calls)."""
     B, Hq, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
