@@ -121,6 +121,21 @@ def test_balanced_schedule_workspace():
     kvp = _kv(batch=16, num_kv_heads=8, max_pages=2048, page_size=32, stride_page=2 * 32 * 128,
               stride_head=32 * 128)
     assert L.bsa_decode_workspace_bytes(ctypes.byref(kvp), 64, 946, 0) == split_bytes
+    # the row limits: 16 to 4096 rows (batch x H_kv)
+    def ws(batch, hkv, hq, items):
+        return L.bsa_decode_workspace_bytes(ctypes.byref(_kv(batch=batch, num_kv_heads=hkv, max_pages=8192)), hq,
+                                            items, 0)
+
+    def grid_bytes(batch, hkv, hq, items):
+        k = _kv(batch=batch, num_kv_heads=hkv, max_pages=8192)
+        s = L.bsa_decode_num_splits(ctypes.byref(k), hq, items, 0)
+        return 0 if s <= 1 else batch * hq * s * 130 * 4
+
+    for batch, hkv, on in ((15, 1, False), (16, 1, True), (512, 8, True), (4097, 1, False)):
+        items = 8192 if batch * hkv < 64 else 64
+        bal = ((batch * hkv + 256) * 1 * 130 * 4 + 15) // 16 * 16 + batch * hkv * (items + 1) * 4
+        want = max(grid_bytes(batch, hkv, hkv, items), bal) if on else grid_bytes(batch, hkv, hkv, items)
+        assert ws(batch, hkv, hkv, items) == want, (batch, hkv)
     # the balanced call checks its own workspace size
     assert _decode(kv, hq=64, splits=0, max_sel=946, ws=FAKE, ws_bytes=bal_bytes - 1) == _abi.BSA_ERR_WORKSPACE
     assert "%d bytes" % bal_bytes in L.bsa_last_error().decode()
