@@ -37,6 +37,11 @@ MUTANTS = {
     "quantile-position": ("double pos = (m - 1) * p;", "double pos = m * p;"),
     "trigger-non-strict": ("triggered[t] = eligible[t] && (sigma_bar[t] < *tau);",
                            "triggered[t] = eligible[t] && (sigma_bar[t] <= *tau);"),
+    "sigma-bar-sum": ("sigma_bar[t] = acc / num_kv_heads;", "sigma_bar[t] = acc;"),
+    "sigma-bar-max-over-heads": ("acc += sigma[(int64_t)t * num_kv_heads + h];\n        sigma_bar[t] = acc / num_kv_heads;",
+                                 "acc = fmax(acc, sigma[(int64_t)t * num_kv_heads + h]);\n        sigma_bar[t] = acc;"),
+    "sigma-bar-first-head": ("sigma_bar[t] = acc / num_kv_heads;", "sigma_bar[t] = sigma[(int64_t)t * num_kv_heads];"),
+    "quantile-over-all-tiles": ("if (eligible[t]) elig_vals[m++] = sigma_bar[t];", "elig_vals[m++] = sigma_bar[t];"),
     "expansion-swapped": ("int keep = triggered[t] ? width : k;", "int keep = triggered[t] ? k : width;"),
     "tile-diagonal-hidden": ("int v = last / block_size + 1;", "int v = last / block_size;"),
     "causal-leak": ("if (p > r) break;", "if (p > r + 1) break;"),

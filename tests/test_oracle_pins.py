@@ -399,6 +399,41 @@ def test_trigger_count(row):
     assert int(r["triggered"].sum()) == want == math.ceil(p * (m - 1))
 
 
+def _router_step4_golden():
+    tiles, quant = [], []
+    for row in _golden("router_step4.txt"):
+        if row[0] == "tile":
+            tiles.append(dict(visible=int(row[1]), scores=[[float(x) for x in row[2].split()],
+                                                           [float(x) for x in row[3].split()]],
+                              sigma=[float(row[4]), float(row[5])], mean=float(row[6]), eligible=bool(int(row[7])),
+                              kv_idx=[[int(x) for x in row[8].split()], [int(x) for x in row[9].split()]]))
+        elif row[0] == "quantile":
+            quant.append((float(row[1]), float(row[2]), sorted(int(x) for x in row[3].split())))
+    return tiles, quant
+
+
+@pytest.mark.parametrize("qrow", range(2))
+def test_router_head_mean_and_eligible_quantile(qrow):
+    """Step 4 of the router on a hand-worked case with two KV heads of
+    different margins and ineligible tiles beside eligible ones: the mean over
+    heads, the quantile over eligible tiles only, the strict trigger and the
+    expansion (tests/golden/router_step4.txt)."""
+    tiles, quant = _router_step4_golden()
+    p, want_tau, want_trig = quant[qrow]
+    ts = np.array([t["scores"] for t in tiles], dtype=np.float64)
+    nv = [t["visible"] for t in tiles]
+    r = oracle.router(ts, nv, 2, 2, quantile_p=p)
+    for i, t in enumerate(tiles):
+        np.testing.assert_allclose(r["sigma"][i], t["sigma"], rtol=0, atol=1e-15)
+        assert abs(r["sigma_bar"][i] - t["mean"]) <= 1e-15
+        assert bool(r["eligible"][i]) == t["eligible"]
+    assert abs(r["tau"] - want_tau) <= 1e-15
+    assert sorted(np.flatnonzero(r["triggered"]).tolist()) == want_trig
+    if p == 0.25:
+        for i, t in enumerate(tiles):
+            assert r["kv_idx"][i].tolist() == t["kv_idx"]
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_router_sets_brute_force_and_prefix(seed):
     g = np.random.default_rng(300 + seed)
