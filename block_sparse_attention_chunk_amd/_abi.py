@@ -43,6 +43,7 @@ SIGNATURES = {
     "bsa_build_chunk_meta": (ctypes.c_int, [_KV, _CH, _MT, _u32, _P]),
     "bsa_update_chunk_meta": (ctypes.c_int, [_KV, _CH, _MT, _u32, _P, _i32, _P]),
     "bsa_score_chunks": (ctypes.c_int, [_P, _i32, _i32, _i32, _KV, _CH, _MT, _i32, _i32, _P, _P]),
+    "bsa_select_max_count": (_i32, [_BG, _i32]),
     "bsa_select_topk": (ctypes.c_int, [_P, _KV, _CH, _BG, _P, _P, _i32, _P]),
     "bsa_router_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "bsa_select_topk_router": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _P, _P, _P, _P,

@@ -268,6 +268,15 @@ int bsa_score_chunks(const void *q, int32_t num_q_heads, int32_t num_rows, int32
                                             (hipStream_t)stream));
 }
 
+int32_t bsa_select_max_count(const bsa_budget *budget, int32_t max_chunks) {
+    if (!budget) return fail(BSA_ERR_INVALID_ARG, "budget is NULL");
+    if (max_chunks < 1) return fail(BSA_ERR_INVALID_ARG, "max_chunks must be >= 1");
+    int64_t need;
+    if (int rc = budget_need(budget, max_chunks, &need)) return rc;
+    ok();
+    return (int32_t)need;
+}
+
 int bsa_select_topk(const float *scores, const bsa_kv *kv, const bsa_chunks *chunks, const bsa_budget *budget,
                     int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *stream) {
     bsa::KvView v;
@@ -357,7 +366,7 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
         return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
     if (num_splits < 0) return fail(BSA_ERR_INVALID_ARG, "num_splits must be >= 0");
     const int items = sel_idx ? max_sel : c.max_chunks;
-    if (out && sel_idx && !chunks && balanced_applies(kv, items, num_splits)) {
+    if (out && sel_idx && !c.starts && balanced_applies(kv, items, num_splits)) {
         const size_t need = balanced_workspace_bytes(kv, num_q_heads);
         if (!workspace || workspace_bytes < need)
             return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need, workspace_bytes);

@@ -75,7 +75,7 @@ void decode_paged16_kernel(const T *__restrict__ q, int hq, KvView kv, const int
     if (items) spec = spec_ld;
     const int L = __builtin_amdgcn_readfirstlane(len_ld);
     const int npages = (L + 15) >> 4;
-    const int nitems = sel_idx ? __builtin_amdgcn_readfirstlane(cnt_ld) : npages;
+    const int nitems = sel_idx ? min(max(__builtin_amdgcn_readfirstlane(cnt_ld), 0), max_sel) : npages;
     WaveState<T, D, GP> st;
     init_state(st);
 
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void decode_chunked_kernel(const T *__restrict
     const int g = hq / kv.hkv;
     const int L = kv.seq_lens[b];
     const int nch = ch.starts ? ch.num[b] : (L + kv.page - 1) >> kv.log2page;
-    const int nitems = sel_idx ? sel_count[(int64_t)b * kv.hkv + h] : nch;
+    const int nitems = sel_idx ? min(max(sel_count[(int64_t)b * kv.hkv + h], 0), max_sel) : nch;
     const int32_t *items = sel_idx ? sel_idx + ((int64_t)b * kv.hkv + h) * max_sel : nullptr;
     const int i0 = (int)((int64_t)split * nitems / splits), i1 = (int)((int64_t)(split + 1) * nitems / splits);
 
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void decode_segments_kernel(const T *__rest
     const int L = kv.seq_lens[b];
     const int nch = ch.starts ? ch.num[b] : (L + kv.page - 1) >> kv.log2page;
     // the kept chunks (<= kSegItems: host-checked against max_sel / max_chunks)
-    const int nitems = min(sel_idx ? min(sel_count[(int64_t)b * kv.hkv + h], max_sel) : nch, kSegItems);
+    const int nitems = min(sel_idx ? min(max(sel_count[(int64_t)b * kv.hkv + h], 0), max_sel) : nch, kSegItems);
     const int32_t *items = sel_idx ? sel_idx + ((int64_t)b * kv.hkv + h) * max_sel : nullptr;
     const int32_t *cs = ch.starts ? ch.starts + (int64_t)b * (ch.max_chunks + 1) : nullptr;
 

@@ -157,12 +157,11 @@ class Budget:
         return _abi.bsa_budget(self.mode, self.top_k, self.tokens, self.bos, self.eos, self.ratio)
 
     def max_selected(self, max_chunks: int) -> int:
-        if self.mode == BSA_BUDGET_TOPK:
-            return min(self.top_k, max_chunks)
-        if self.mode == BSA_BUDGET_TOKENS:
-            return min(self.tokens, max_chunks)
-        K = max(1 + self.bos + self.eos, int(math.floor(max_chunks * self.ratio)))
-        return min(K, max_chunks)
+        """bsa_select_max_count: the largest selection a row of max_chunks
+        candidates can keep under this budget (the size of max_sel)."""
+        n = int(_abi.lib().bsa_select_max_count(ctypes.byref(self.struct()), int(max_chunks)))
+        _abi.check(min(n, 0), "bsa_select_max_count")
+        return n
 
 
 def build_chunk_meta(kv: KVCache, chunks: Optional[Chunks] = None, which: int = BSA_META_ENVELOPE | BSA_META_CENTROID,

@@ -190,6 +190,17 @@ int bsa_score_chunks(const void *q, int32_t num_q_heads, int32_t num_rows, int32
  * TOKENS: min(tokens, max_chunks)).  max_chunks <= 8192.
  * Errors: INVALID_ARG (budget values, max_sel too small), UNSUPPORTED.
  */
+/*
+ * The largest number of chunks a row of max_chunks candidates can keep under
+ * `budget` [host]: the size max_sel must have for bsa_select_topk and
+ * bsa_select_attn_decode.  TOPK: min(top_k, max_chunks) ([P1] budget =
+ * page_size x top_k).  TOKENS: min(tokens, max_chunks) (every kept chunk holds
+ * at least one token).  RATIO ([P2] "Method configurations at a glance"):
+ * min(max_chunks, max(1 + bos + eos, floor(max_chunks * ratio))).
+ * Returns the count (>= 1), or a negative BSA_ERR_* code for an invalid budget
+ * or max_chunks < 1 (bsa_last_error() describes it).  Host only; no HIP call.
+ */
+int32_t bsa_select_max_count(const bsa_budget *budget /* [host] */, int32_t max_chunks);
 int bsa_select_topk(const float *scores, const bsa_kv *kv, const bsa_chunks *chunks /* nullable */,
                     const bsa_budget *budget /* [host] */, int32_t *sel_idx, int32_t *sel_count, int32_t max_sel,
                     void *stream);
@@ -233,12 +244,13 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * Group size H_q/H_kv <= 16.  workspace >= bsa_decode_workspace_bytes(...)
  * (0 bytes when the resolved split count is 1 and the balanced schedule below
  * does not apply): the partials, merged by a second kernel on the same
- * stream.  Splits are capped at 64.  Calls that
- * share a workspace must not overlap.  sel_count entries must not exceed
- * max_sel.  With more than one split, out may be NULL: the merge is skipped
- * and the workspace holds the partials (layout at bsa_decode_merge).
- * Balanced schedule: with num_splits == 0, out != NULL, a selection, no chunk
- * list, 16-token pages, 16 <= batch x H_kv <= 4096 and batch x H_kv x max_sel
+ * stream.  Splits are capped at 64.  Calls that share a workspace must not
+ * overlap.  sel_count entries are clamped to [0, max_sel] by every schedule
+ * (the first max_sel entries are attended).  With more than one split, out
+ * may be NULL: the merge is skipped and the workspace holds the partials
+ * (layout at bsa_decode_merge).
+ * Balanced schedule: with num_splits == 0, out != NULL, a selection, fixed
+ * pages (chunks NULL or chunks->chunk_starts NULL), 16-token pages, 16 <= batch x H_kv <= 4096 and batch x H_kv x max_sel
  * >= 49152, the kept pages of all rows are laid end to end and cut into 256
  * equal shares, one workgroup each, instead of a fixed split count per row
  * (rows of unequal length then keep every compute unit busy to the end).

@@ -69,9 +69,10 @@ def oracle_select(scores, case, budget):
                 chunk_len[b, c] = min(case.page_size, L - c * case.page_size)
     mode = {ops.BSA_BUDGET_TOPK: oracle.TOPK, ops.BSA_BUDGET_TOKENS: oracle.TOKENS,
             ops.BSA_BUDGET_RATIO: oracle.RATIO}[budget.mode]
-    max_sel = budget.max_selected(case.max_chunks)
+    # rows as wide as the whole candidate list: the oracle's buffer size owes
+    # nothing to the library's sizing rule; counts are compared, not widths
     return oracle.select(scores, n, mode, top_k=budget.top_k, tokens=budget.tokens, ratio=budget.ratio,
-                         bos=budget.bos, eos=budget.eos, chunk_len=chunk_len, max_sel=max_sel)
+                         bos=budget.bos, eos=budget.eos, chunk_len=chunk_len, max_sel=case.max_chunks)
 
 
 def check_scores(gpu, ref, den, n_chunks, what):

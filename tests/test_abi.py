@@ -139,11 +139,50 @@ def test_balanced_schedule_workspace():
     # the balanced call checks its own workspace size
     assert _decode(kv, hq=64, splits=0, max_sel=946, ws=FAKE, ws_bytes=bal_bytes - 1) == _abi.BSA_ERR_WORKSPACE
     assert "%d bytes" % bal_bytes in L.bsa_last_error().decode()
+    # a chunk struct without chunk_starts means fixed pages: the same schedule
+    empty = _abi.bsa_chunks(None, None, 0)
+    rc = L.bsa_sparse_attn_decode(FAKE, 64, ctypes.byref(kv), ctypes.byref(empty), FAKE, FAKE, 946, 0.088, 0, FAKE,
+                                  FAKE, bal_bytes - 1, None)
+    assert rc == _abi.BSA_ERR_WORKSPACE
+    assert "%d bytes" % bal_bytes in L.bsa_last_error().decode()
 
 
 def _select(kv, budget, max_sel, chunks=None):
     L = _abi.lib()
     return L.bsa_select_topk(FAKE, ctypes.byref(kv), chunks, ctypes.byref(budget), FAKE, FAKE, max_sel, None)
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([c.strip() for c in line.split(";")])
+    return rows
+
+
+def test_select_max_count_matches_the_ratio_budget_table():
+    """bsa_select_max_count against the worked ratio-budget values
+    (tests/golden/ratio_budget.txt), plus the top-k and token rules."""
+    L = _abi.lib()
+    B = _abi.bsa_budget
+    rows = _golden("ratio_budget.txt")
+    assert len(rows) >= 10
+    for n, ratio, bos, eos, want in rows:
+        b = B(_abi.BSA_BUDGET_RATIO, 0, 0, int(bos), int(eos), float(ratio))
+        assert L.bsa_select_max_count(ctypes.byref(b), int(n)) == int(want), (n, ratio, bos, eos)
+    assert L.bsa_select_max_count(ctypes.byref(B(_abi.BSA_BUDGET_TOPK, 256, 0, 0, 0, 0.0)), 1844) == 256
+    assert L.bsa_select_max_count(ctypes.byref(B(_abi.BSA_BUDGET_TOPK, 256, 0, 0, 0, 0.0)), 100) == 100
+    assert L.bsa_select_max_count(ctypes.byref(B(_abi.BSA_BUDGET_TOKENS, 0, 4096, 0, 0, 0.0)), 221) == 221
+    assert L.bsa_select_max_count(ctypes.byref(B(_abi.BSA_BUDGET_TOKENS, 0, 40, 0, 0, 0.0)), 221) == 40
+    # invalid budgets and sizes give error codes with a message
+    for bad, n in [(B(_abi.BSA_BUDGET_TOPK, 0, 0, 0, 0, 0.0), 10), (B(_abi.BSA_BUDGET_RATIO, 0, 0, 0, 1, 0.0), 10),
+                   (B(_abi.BSA_BUDGET_RATIO, 0, 0, 2, 1, 0.5), 10), (B(9, 1, 0, 0, 0, 0.0), 10),
+                   (B(_abi.BSA_BUDGET_TOPK, 4, 0, 0, 0, 0.0), 0)]:
+        assert L.bsa_select_max_count(ctypes.byref(bad), n) == _abi.BSA_ERR_INVALID_ARG
+        assert L.bsa_last_error()
+    assert L.bsa_select_max_count(None, 10) == _abi.BSA_ERR_INVALID_ARG
 
 
 def test_select_argument_checks():

@@ -259,14 +259,27 @@ def test_deterministic_bits(dev):
     assert np.array_equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("ratio", [0.5, 0.125])
-def test_batched_ratio_full_size(dev, ratio):
+@pytest.mark.parametrize("kind,ratio", [("centroid", 0.5), ("centroid", 0.125), ("envelope", 0.5),
+                                        ("envelope", 0.0625)])
+def test_batched_ratio_full_size(dev, kind, ratio):
     """16 sequences with lengths in [8192, 32768], 64 q / 8 KV heads (the
-    benchmark's batched workload) at two ratios, centroid with bos+eos."""
+    benchmark's batched workload): centroid scoring with bos + eos forced,
+    envelope scoring with eos only (bos = 0), at the largest ratio and a
+    small one; kept counts follow the ratio formula."""
     from block_sparse_attention_chunk_amd import ops
     case = synth.batched_decode()
-    run_decode_case(case, dev, ops.BSA_CENTROID, ops.Budget.ratio_budget(ratio, 1, 1), forced=("bos", "eos"),
-                    check_dense=ratio == 0.125)
+    bos = 1 if kind == "centroid" else 0
+    kd = ops.BSA_CENTROID if kind == "centroid" else ops.BSA_ENVELOPE
+    forced = (("bos",) if bos else ()) + ("eos",)
+    r = run_decode_case(case, dev, kd, ops.Budget.ratio_budget(ratio, bos, 1), forced=forced,
+                        check_dense=ratio == 0.125)
+    n = case.n_chunks()
+    for b in range(case.batch):
+        K = min(int(n[b]), max(2 + bos, int(math.floor(int(n[b]) * ratio))))
+        assert np.all(r["cnt"][b] == K)
+        for h in range(case.num_kv_heads):
+            s = r["sel"][b, h, :K]
+            assert int(n[b]) - 1 in s and (not bos or 0 in s)
 
 
 @pytest.mark.parametrize("dtype,D,hq", [("bf16", 128, 8), ("f32", 64, 8), ("bf16", 64, 32), ("f32", 128, 32)])

@@ -1,12 +1,14 @@
-"""Incremental chunk metadata (bsa_update_chunk_meta) against a full rebuild
-(bsa_build_chunk_meta, itself oracle-checked in the decode parity tests):
-after appending tokens -- one at a time, or several at once -- every chunk's
-kmin / kmax / centroid must be bit-identical to a rebuild at the new length.
-Fixed 16-token pages with a shuffled block table, and variable chunks whose
-last chunk grows."""
+"""Incremental chunk metadata (bsa_update_chunk_meta): after appending
+tokens -- one at a time, or several at once -- every chunk's kmin / kmax /
+centroid must be bit-identical to a full rebuild at the new length
+(bsa_build_chunk_meta) and must match the oracle's metadata at the new length
+directly (kmin / kmax bit-exact, centroid within the float32 summation
+bound).  Fixed 16-token pages with a shuffled block table, and variable
+chunks whose last chunk grows."""
 import numpy as np
 import pytest
 
+import oracle
 from block_sparse_attention_chunk_amd import synth
 from parity_lib import log
 
@@ -35,6 +37,29 @@ def _same(a, b, n):
             assert torch.equal(x[bi, :, :nb], y[bi, :, :nb])
 
 
+def _vs_oracle(meta, case, lens, starts=None, num=None):
+    """The updated metadata against the oracle's metadata of the grown cache."""
+    oc = oracle.PagedCache(case.k, case.v, case.block_table, lens, case.page_size, case.num_kv_heads, case.head_dim)
+    omin, omax, ocen = oracle.chunk_meta(oc, starts, num)
+    kmin, kmax = oracle.to_f64(_host(meta.kmin)), oracle.to_f64(_host(meta.kmax))
+    cen = meta.centroid.cpu().numpy()
+    kabs = float(np.nanmax(np.abs(oracle.to_f64(case.k))))
+    longest = case.page_size if starts is None else int(np.max(np.diff(starts, axis=1)))
+    tol = (longest + 1) * 2.0 ** -24 * kabs
+    n = (np.asarray(lens) + case.page_size - 1) // case.page_size if starts is None else np.asarray(num)
+    for b, nb in enumerate(n):
+        nb = int(nb)
+        assert np.array_equal(kmin[b, :, :nb], omin[b, :, :nb]), f"kmin of sequence {b} differs from the oracle"
+        assert np.array_equal(kmax[b, :, :nb], omax[b, :, :nb]), f"kmax of sequence {b} differs from the oracle"
+        assert np.max(np.abs(cen[b, :, :nb] - ocen[b, :, :nb])) <= tol, f"centroid of sequence {b}"
+
+
+def _host(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
 def test_append_one_token_at_a_time(dev):
     from block_sparse_attention_chunk_amd import ops
     case = synth.make_decode(50, batch=3, seq_lens=[100, 513, 1040], num_q_heads=8, num_kv_heads=2, head_dim=128,
@@ -51,6 +76,7 @@ def test_append_one_token_at_a_time(dev):
     ref = ops.build_chunk_meta(_kv(ops, case, dev, L))
     torch.cuda.synchronize()
     _same(meta, ref, (L + 15) // 16)
+    _vs_oracle(meta, case, L)
 
 
 @pytest.mark.parametrize("dtype_f32", [False, True])
@@ -69,6 +95,7 @@ def test_append_many_tokens(dev, dtype_f32):
     ref = ops.build_chunk_meta(kv)
     torch.cuda.synchronize()
     _same(meta, ref, (L + 15) // 16)
+    _vs_oracle(meta, case, L)
 
 
 def test_variable_chunks_last_chunk_grows(dev):
@@ -92,3 +119,4 @@ def test_variable_chunks_last_chunk_grows(dev):
     ref = ops.build_chunk_meta(kv, ch)
     torch.cuda.synchronize()
     _same(meta, ref, [n])
+    _vs_oracle(meta, case, [L], starts, case.num_chunks)

@@ -80,6 +80,44 @@ def check_router_on_gpu_scores(g, n_tiles, k, rho):
     return ref, m
 
 
+def check_router_end_to_end(g, ots, oden, k, rho, quantile=0.25):
+    """The GPU pipeline's router against the oracle's own pipeline (oracle
+    metadata, oracle tile scores, oracle router).  Each GPU tile score may sit
+    up to SCORE_REL * D from the oracle's, and order statistics move no more
+    than their inputs, so s_(0), s_(k-1), s_(k) each move by at most
+    delta = SCORE_REL * max D over the visible blocks; then
+      |sigma' - sigma| <= 4 delta / (s_(0) - s_(k) - 2 delta)  (+1e-6 for fp32),
+    sigma_bar moves by at most the mean of its heads' bounds, and the
+    threshold, an interpolation of two order statistics of sigma_bar, by at
+    most the largest of those.  sigma and tau are gated within these bounds,
+    and the trigger set must be exact for every tile whose |sigma_bar - tau|
+    exceeds its own bound plus tau's.  Returns (gated tiles, eligible tiles)."""
+    n_tiles, H, nb = ots.shape
+    nv = np.minimum(np.arange(n_tiles) + 1, nb)
+    full = oracle.router(ots, nv, k, rho, quantile_p=quantile)
+    eps = np.zeros((n_tiles, H))
+    for t in range(n_tiles):
+        n = int(nv[t])
+        if n <= k:
+            continue                              # sigma = 1 on both sides, not eligible
+        for h in range(H):
+            srt = np.sort(ots[t, h, :n])[::-1]
+            delta = SCORE_REL * float(oden[t, h, :n].max())
+            gap = srt[0] - srt[k] - 2.0 * delta
+            eps[t, h] = 4.0 * delta / gap + 1e-6 if gap > 0 else np.inf
+    elig = full["eligible"]
+    assert np.array_equal(elig, nv > k)
+    fin = np.isfinite(eps)
+    assert np.all(np.abs(g["sigma"][fin] - full["sigma"][fin]) <= eps[fin])
+    eps_bar = eps.mean(axis=1)
+    eps_tau = float(eps_bar[elig].max()) if elig.any() else 0.0
+    assert abs(g["tau"] - full["tau"]) <= eps_tau
+    clear = np.abs(full["sigma_bar"] - full["tau"]) > eps_bar + eps_tau
+    assert np.array_equal(g["triggered"][clear], full["triggered"][clear]), \
+        f"trigger differs from the oracle pipeline on tiles {np.flatnonzero(clear & (g['triggered'] != full['triggered']))}"
+    return int((clear & elig).sum()), int(elig.sum())
+
+
 @pytest.mark.parametrize("kind", ["envelope", "centroid"])
 def test_router_prefill_small(dev, kind):
     from block_sparse_attention_chunk_amd import ops
@@ -119,11 +157,11 @@ def test_router_prefill_small(dev, kind):
     dref = oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=4, block_size=64, tile_rows=64, rows=rows)
     de = max_abs(_np(dout)[rows], dref)
     assert de <= ATTN_ABS["bf16"], de
-    # end to end against the oracle's own pipeline (reported; stage parity is gated above)
-    full = oracle.router(ots, np.minimum(np.arange(n_tiles) + 1, n_tiles), k, rho)
-    agree = float(np.mean(full["triggered"] == g["triggered"]))
+    # end to end against the oracle's own pipeline, outside the propagated band
+    gated, elig = check_router_end_to_end(g, ots, oden, k, rho)
+    assert gated >= elig // 2, (gated, elig)
     log(f"  ok: tile score err {err.max():.2e} D, attn err {e:.2e}, dense err {de:.2e}, m={m}, "
-        f"trigger agreement with the all-oracle pipeline {agree:.3f}")
+        f"trigger set exact against the all-oracle pipeline on {gated} of {elig} eligible tiles")
 
 
 @pytest.mark.parametrize("quantile,fixed,rho", [(0.0, None, 2), (1.0, None, 2), (0.5, None, 3), (0.25, 0.3, 2),
@@ -184,23 +222,59 @@ def test_router_prefill_ragged(dev):
     assert np.array_equal(np.isfinite(g["ts"]), vis)
     assert (np.abs(g["ts"][vis] - ots[vis]) / oden[vis]).max() <= SCORE_REL
     check_router_on_gpu_scores(g, n_tiles, 4, 2)
+    check_router_end_to_end(g, ots, oden, 4, 2)
     ref_o = oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=2, block_size=64, tile_rows=64, kv_idx=g["kv_idx"])
     assert max_abs(_np(out), ref_o) <= ATTN_ABS["bf16"]
     dref = oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=2, block_size=64, tile_rows=64)
     assert max_abs(_np(dout), dref) <= ATTN_ABS["bf16"]
 
 
-def test_router_prefill_full_size(dev):
-    """131,072 tokens, 28 q / 4 KV heads, k = 32, rho = 2, quantile 0.25: every
-    GPU stage runs at full size; the oracle checks sampled tiles and rows and
-    recomputes the whole router from the GPU's tile scores."""
+@pytest.mark.parametrize("kind", ["envelope", "centroid"])
+def test_router_prefill_16k_end_to_end(dev, kind):
+    """16,384 tokens (256 tiles), 28 q / 4 KV heads, k = 32, rho = 2: the
+    whole router against the all-oracle pipeline (oracle metadata, every tile
+    score, router), gated outside the propagated band, and sampled rows of the
+    attention."""
     from block_sparse_attention_chunk_amd import ops
     k, rho = 32, 2
-    log("router prefill full size: generating inputs")
+    pc = synth.router_prefill(cid=106, T=16384, k=k, groups=2, tied_groups=(1,))
+    kd = ops.BSA_ENVELOPE if kind == "envelope" else ops.BSA_CENTROID
+    log(f"router prefill 16K {kind}")
+    g, out, _ = gpu_prefill(pc, dev, kd, k, rho)
+    omin, omax, ocen = block_meta_oracle(pc)
+    assert np.array_equal(oracle.to_f64(g["kmin"]), omin) and np.array_equal(oracle.to_f64(g["kmax"]), omax)
+    okind = oracle.ENVELOPE if kind == "envelope" else oracle.CENTROID
+    ots, oden = oracle.tile_scores(pc.q, (omin, omax, ocen), okind, num_kv_heads=4, tile_rows=64, block_size=64)
+    vis = np.isfinite(ots)
+    assert np.array_equal(np.isfinite(g["ts"]), vis)
+    err = (np.abs(g["ts"][vis] - ots[vis]) / oden[vis]).max()
+    assert err <= SCORE_REL, err
+    check_router_on_gpu_scores(g, pc.T // pc.tile, k, rho)
+    gated, elig = check_router_end_to_end(g, ots, oden, k, rho)
+    assert gated >= elig // 3, (gated, elig)
+    rows = np.array([0, 63, 64, 2047, 2048, 5000, 9999, 16383])
+    ref_o = oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=4, block_size=64, tile_rows=64, kv_idx=g["kv_idx"],
+                             rows=rows)
+    e = max_abs(_np(out)[rows], ref_o)
+    assert e <= ATTN_ABS["bf16"], e
+    log(f"  ok: score err {err:.2e} D, trigger set exact on {gated} of {elig} eligible tiles, attn err {e:.2e}")
+
+
+@pytest.mark.parametrize("kind", ["envelope", "centroid"])
+def test_router_prefill_full_size(dev, kind):
+    """131,072 tokens, 28 q / 4 KV heads, k = 32, rho = 2, quantile 0.25, both
+    scoring backbones: every GPU stage runs at full size; the oracle checks
+    sampled blocks, tiles and rows and recomputes the whole router from the
+    GPU's tile scores."""
+    from block_sparse_attention_chunk_amd import ops
+    k, rho = 32, 2
+    log(f"router prefill full size ({kind}): generating inputs")
     pc = synth.router_prefill()
     n_tiles = pc.T // pc.tile
     log("  running the GPU pipeline")
-    g, out, _ = gpu_prefill(pc, dev, ops.BSA_ENVELOPE, k, rho)
+    kd = ops.BSA_ENVELOPE if kind == "envelope" else ops.BSA_CENTROID
+    okind = oracle.ENVELOPE if kind == "envelope" else oracle.CENTROID
+    g, out, _ = gpu_prefill(pc, dev, kd, k, rho)
     o = _np(out)
     del out
     # metadata of sampled blocks
@@ -211,11 +285,13 @@ def test_router_prefill_full_size(dev):
         seg = kk[b * 64:(b + 1) * 64]
         assert np.array_equal(oracle.to_f64(g["kmin"])[0, :, b], seg.min(axis=0))
         assert np.array_equal(oracle.to_f64(g["kmax"])[0, :, b], seg.max(axis=0))
+        cen_tol = 65 * 2.0 ** -24 * float(np.abs(seg).max())
+        assert np.max(np.abs(g["cen"][0, :, b] - seg.mean(axis=0))) <= cen_tol
     # tile scores of sampled tiles
     tiles = np.array([0, 31, 32, 33, 400, 1024, 2047])
     log("  oracle tile scores on sampled tiles")
     meta = (oracle.to_f64(g["kmin"]), oracle.to_f64(g["kmax"]), g["cen"].astype(np.float64))
-    ots, oden = oracle.tile_scores(pc.q, meta, oracle.ENVELOPE, num_kv_heads=4, tile_rows=64, block_size=64,
+    ots, oden = oracle.tile_scores(pc.q, meta, okind, num_kv_heads=4, tile_rows=64, block_size=64,
                                    tiles=tiles)
     for i, t in enumerate(tiles):
         vis = np.isfinite(ots[i])

@@ -61,16 +61,16 @@ def test_selection_with_ties_is_exact(dev, n_max, mode):
                      torch.zeros((B, n_max), dtype=torch.int32, device=dev))
     if mode == "topk":
         bud = ops.Budget.topk(max(1, n_max // 7))
-        ref = oracle.select(sc.astype(np.float64), n, oracle.TOPK, top_k=bud.top_k, max_sel=bud.max_selected(n_max))
+        ref = oracle.select(sc.astype(np.float64), n, oracle.TOPK, top_k=bud.top_k, max_sel=n_max)
     elif mode == "tokens":
         bud = ops.Budget.token_budget(n_max * 3 + 5)
         ref = oracle.select(sc.astype(np.float64), n, oracle.TOKENS, tokens=bud.tokens,
-                            chunk_len=_chunk_len(n, lens, n_max), max_sel=bud.max_selected(n_max))
+                            chunk_len=_chunk_len(n, lens, n_max), max_sel=n_max)
     else:
         bos = 1 if mode == "ratio_bos_eos" else 0
         bud = ops.Budget.ratio_budget(0.125, bos, 1)
         ref = oracle.select(sc.astype(np.float64), n, oracle.RATIO, ratio=0.125, bos=bos, eos=1,
-                            max_sel=bud.max_selected(n_max))
+                            max_sel=n_max)
     scores = torch.tensor(sc, device=dev)
     sel, cnt = ops.select_topk(scores, kv, bud)
     # the fused selection + attention writes the same kept list: a small grid
