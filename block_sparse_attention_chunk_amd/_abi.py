@@ -12,6 +12,7 @@ BSA_F32, BSA_BF16 = 0, 1
 BSA_ENVELOPE, BSA_CENTROID = 0, 1
 BSA_META_ENVELOPE, BSA_META_CENTROID = 1, 2
 BSA_BUDGET_TOPK, BSA_BUDGET_TOKENS, BSA_BUDGET_RATIO = 0, 1, 2
+BSA_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class bsa_kv(ctypes.Structure):
@@ -53,6 +54,7 @@ SIGNATURES = {
     "bsa_sparse_attn_decode": (ctypes.c_int, [_P, _i32, _KV, _CH, _P, _P, _i32, _f32, _i32, _P, _P, _sz, _P]),
     "bsa_decode_merge": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32, _P, _P]),
     "bsa_select_attn_decode": (ctypes.c_int, [_P, _i32, _KV, _P, _BG, _f32, _i32, _P, _P, _P, _i32, _P, _sz, _P]),
+    "bsa_select_attn_decode_static": (ctypes.c_int, [_P, _i32, _KV, _P, _BG, _f32, _i32, _P, _P, _P, _i32, _P]),
     "bsa_tile_prefill_workspace_bytes": (ctypes.c_size_t, [_KV, _i32]),
     "bsa_sparse_attn_tile_prefill": (ctypes.c_int, [_P, _i32, _i32, _KV, _i32, _P, _i32, _f32, _P, _P, ctypes.c_size_t,
                                                     _P]),

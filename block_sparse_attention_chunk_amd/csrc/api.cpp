@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "bsa_internal.h"
 
@@ -386,12 +387,21 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
                                        workspace, (hipStream_t)stream));
 }
 
-int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
-                           const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
-                           int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+// The fused decode call's host side: every argument check and the launch
+// plan, without a HIP call, so the no-allocation variant can size its scratch
+// before touching the device.
+struct FusedPlan {
     bsa::KvView v;
-    int rc = check_kv(kv, true, &v);
+    int64_t need;       // the largest possible selection K
+    bool balanced;      // selection kernel + balanced attention instead of the fused kernel
+    int splits;         // the fused kernel's split count
+    size_t ws_need;     // workspace bytes the launch uses
+};
+
+static int plan_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
+                                   const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
+                                   int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, FusedPlan *p) {
+    int rc = check_kv(kv, true, &p->v);
     if (rc) return rc;
     if ((rc = check_heads(kv, num_q_heads, 16))) return rc;
     if (!q || !scores || !budget) return fail(BSA_ERR_INVALID_ARG, "q, scores and budget must be non-NULL");
@@ -402,51 +412,124 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
         return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
     if (num_splits < 0 || num_splits > 64) return fail(BSA_ERR_INVALID_ARG, "num_splits must be in [0, 64]");
-    int64_t need;
-    if ((rc = budget_need(budget, kv->max_pages, &need))) return rc;
+    if ((rc = budget_need(budget, kv->max_pages, &p->need))) return rc;
     if ((sel_idx == nullptr) != (sel_count == nullptr))
         return fail(BSA_ERR_INVALID_ARG, "sel_idx and sel_count are both given or both NULL");
-    if (sel_idx && max_sel < need)
+    if (sel_idx && max_sel < p->need)
         return fail(BSA_ERR_INVALID_ARG, "max_sel %d is smaller than the largest possible selection %lld", max_sel,
-                    (long long)need);
-    if (out && balanced_applies(kv, (int)need, num_splits)) {
+                    (long long)p->need);
+    if (out && !aligned16(out)) return fail(BSA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    p->balanced = out && balanced_applies(kv, (int)p->need, num_splits);
+    if (p->balanced) {
+        p->splits = 0;
+        p->ws_need = balanced_workspace_bytes(kv, num_q_heads) + (sel_idx ? 0 : balanced_list_bytes(kv, (int)p->need));
+        return BSA_OK;
+    }
+    p->splits = resolve_splits(kv, (int)p->need, num_splits);
+    if ((p->need + p->splits - 1) / p->splits > kMaxItemsPerSplit)
+        return fail(BSA_ERR_INVALID_ARG, "%d splits keep more than %d pages each; use more splits", p->splits,
+                    kMaxItemsPerSplit);
+    if (!out && p->splits == 1)
+        return fail(BSA_ERR_INVALID_ARG, "out may be NULL only with more than one split (partials stay in the "
+                                         "workspace)");
+    p->ws_need = bsa_decode_workspace_bytes(kv, num_q_heads, (int)p->need, p->splits);
+    return BSA_OK;
+}
+
+// Enqueues a planned fused decode call; the workspace (16-byte aligned, at
+// least p.ws_need bytes when p.ws_need > 0) has been checked by the caller.
+static int launch_select_attn_decode(const FusedPlan &p, const void *q, int32_t num_q_heads, const bsa_kv *kv,
+                                     const float *scores, const bsa_budget *budget, float softmax_scale, float *out,
+                                     int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace,
+                                     void *stream) {
+    if (p.balanced) {
         // a large batch: the selection kernel, then the attention on the
         // balanced schedule (the same kernels and bits as the two calls)
         const size_t part = balanced_workspace_bytes(kv, num_q_heads);
-        const size_t ws_need = part + (sel_idx ? 0 : balanced_list_bytes(kv, (int)need));
-        if (!workspace || workspace_bytes < ws_need)
-            return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", ws_need, workspace_bytes);
-        if ((rc = check_out_ws(out, workspace))) return rc;
         const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
         int32_t *si = sel_idx, *sc = sel_count;
         int32_t ms = max_sel;
         if (!si) {
             si = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + part);
-            sc = si + rows * need;
-            ms = (int32_t)need;
+            sc = si + rows * p.need;
+            ms = (int32_t)p.need;
         }
         bsa::ChunkView c;
         check_chunks(kv, nullptr, &c);
-        hipError_t e = bsa::launch_select(scores, v, c, *budget, si, sc, ms, (hipStream_t)stream);
+        hipError_t e = bsa::launch_select(scores, p.v, c, *budget, si, sc, ms, (hipStream_t)stream);
         if (e == hipSuccess)
-            e = bsa::launch_decode_balanced(q, num_q_heads, v, si, sc, ms, softmax_scale, out, workspace,
+            e = bsa::launch_decode_balanced(q, num_q_heads, p.v, si, sc, ms, softmax_scale, out, workspace,
                                             (hipStream_t)stream);
         return launched(e);
     }
-    const int splits = resolve_splits(kv, (int)need, num_splits);
-    if ((need + splits - 1) / splits > kMaxItemsPerSplit)
-        return fail(BSA_ERR_INVALID_ARG, "%d splits keep more than %d pages each; use more splits", splits,
-                    kMaxItemsPerSplit);
-    if (!out && splits == 1)
-        return fail(BSA_ERR_INVALID_ARG, "out may be NULL only with more than one split (partials stay in the "
-                                         "workspace)");
-    const size_t ws_need = bsa_decode_workspace_bytes(kv, num_q_heads, (int)need, splits);
-    if (ws_need && (!workspace || workspace_bytes < ws_need))
-        return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", ws_need, workspace_bytes);
-    if ((rc = check_out_ws(out, ws_need ? workspace : nullptr))) return rc;
-    return launched(bsa::launch_select_decode(q, num_q_heads, v, scores, *budget, sel_idx, sel_count,
-                                              sel_idx ? max_sel : 0, softmax_scale, splits, out, workspace,
-                                              (hipStream_t)stream));
+    return launched(bsa::launch_select_decode(q, num_q_heads, p.v, scores, *budget, sel_idx, sel_count,
+                                              sel_idx ? max_sel : 0, softmax_scale, p.splits, out,
+                                              p.ws_need ? workspace : nullptr, (hipStream_t)stream));
+}
+
+int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
+                           const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
+                           int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    FusedPlan p;
+    int rc = plan_select_attn_decode(q, num_q_heads, kv, scores, budget, softmax_scale, num_splits, out, sel_idx,
+                                     sel_count, max_sel, &p);
+    if (rc) return rc;
+    if (p.ws_need && (!workspace || workspace_bytes < p.ws_need))
+        return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", p.ws_need, workspace_bytes);
+    if (p.ws_need && !aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return launch_select_attn_decode(p, q, num_q_heads, kv, scores, budget, softmax_scale, out, sel_idx, sel_count,
+                                     max_sel, workspace, stream);
+}
+
+// ---- the no-allocation fused decode entry point -------------------------------
+// Device scratch for bsa_select_attn_decode_static: one copy of this array per
+// GPU, loaded with the library's code object and held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address); it takes each device's address once, from
+// hipGetSymbolAddress, and uses that pointer.
+static __device__ __align__(256) unsigned char scratch[BSA_STATIC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[64] = {};
+
+// The scratch address on the current device, taken on the first call there.
+static int scratch_on_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(BSA_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(BSA_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(BSA_ERR_LAUNCH, "hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return BSA_OK;
+}
+
+int bsa_select_attn_decode_static(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
+                                  const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
+                                  int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *stream) {
+    if (!out) return fail(BSA_ERR_INVALID_ARG, "out must be non-NULL (partials in the static scratch are not "
+                                               "reachable by the caller)");
+    FusedPlan p;
+    int rc = plan_select_attn_decode(q, num_q_heads, kv, scores, budget, softmax_scale, num_splits, out, sel_idx,
+                                     sel_count, max_sel, &p);
+    if (rc) return rc;
+    if (p.ws_need > (size_t)BSA_STATIC_SCRATCH_BYTES)
+        return fail(BSA_ERR_UNSUPPORTED,
+                    "this call needs %zu bytes of scratch; the static scratch holds %zu (use bsa_select_attn_decode "
+                    "with a workspace)",
+                    p.ws_need, (size_t)BSA_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (p.ws_need && (rc = scratch_on_current_device(&ws))) return rc;
+    return launch_select_attn_decode(p, q, num_q_heads, kv, scores, budget, softmax_scale, out, sel_idx, sel_count,
+                                     max_sel, ws, stream);
 }
 
 int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, int32_t head_dim,

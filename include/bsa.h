@@ -309,6 +309,29 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
                            size_t workspace_bytes, void *stream);
 
 /*
+ * bsa_select_attn_decode for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, kernels and bits,
+ * with the scratch taken from a static device array of
+ * BSA_STATIC_SCRATCH_BYTES in the library (one per GPU, held until the
+ * process ends).  The call makes no allocation.  It runs on the CURRENT
+ * device (the one `stream` belongs to); the first call on a device looks up
+ * that device's copy of the array.  Calls on one GPU share its array and
+ * race if they overlap (in time, on any streams): serialise them.  No
+ * kernel of this call needs the array cleared.  out must be given (partials
+ * left in the array would be out of the caller's reach).  A call whose
+ * scratch need (bsa_decode_workspace_bytes for its plan) exceeds
+ * BSA_STATIC_SCRATCH_BYTES is refused with BSA_ERR_UNSUPPORTED before any
+ * HIP call.
+ * Errors: as bsa_select_attn_decode, INVALID_ARG (out NULL), UNSUPPORTED
+ * (scratch too small).
+ */
+#define BSA_STATIC_SCRATCH_BYTES (16u << 20)
+int bsa_select_attn_decode_static(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
+                                  const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
+                                  int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *stream);
+
+/*
  * Step 5 attention ([P3] step 5): causal prefill over query tiles of
  * tile_rows rows.  Row r of tile t, query head j, attends to the keys of the
  * non-sentinel blocks in kv_idx[t][j / (H_q/H_kv)] (idx_stride entries per

@@ -351,3 +351,28 @@ def test_decode_outputs_must_be_16_byte_aligned():
     # merge
     assert L.bsa_decode_merge(FAKE + 4, 1, 8, 128, 4, FAKE, None) == _abi.BSA_ERR_INVALID_ARG
     assert L.bsa_decode_merge(FAKE, 1, 8, 128, 4, FAKE + 8, None) == _abi.BSA_ERR_INVALID_ARG
+
+
+def test_static_scratch_entry_point_refuses_before_any_hip_call():
+    """bsa_select_attn_decode_static checks its arguments and its scratch need
+    on the host: out NULL and a plan needing more than the static scratch are
+    refused without a device."""
+    L = _abi.lib()
+    top = _abi.bsa_budget(_abi.BSA_BUDGET_TOPK, 8, 0, 0, 0, 0.0)
+
+    def call(kv, hq, budget=top, out=FAKE):
+        return L.bsa_select_attn_decode_static(FAKE, hq, ctypes.byref(kv), FAKE, ctypes.byref(budget), 0.088, 0,
+                                               out, None, None, 0, None)
+
+    assert call(_kv(), 8, out=None) == _abi.BSA_ERR_INVALID_ARG
+    assert "out" in L.bsa_last_error().decode()
+    assert call(_kv(page_size=32, stride_page=2 * 32 * 128, stride_head=32 * 128), 8) == _abi.BSA_ERR_UNSUPPORTED
+    # 4096 rows, groups of 16 heads, balanced schedule: (4096 + 256) x 16 x 130
+    # floats of partials alone exceed 16 MiB
+    big = _kv(batch=4096, num_kv_heads=1, max_pages=64)
+    top64 = _abi.bsa_budget(_abi.BSA_BUDGET_TOPK, 64, 0, 0, 0, 0.0)
+    need = L.bsa_decode_workspace_bytes(ctypes.byref(big), 16, 64, 0)
+    assert need > _abi.BSA_STATIC_SCRATCH_BYTES
+    assert call(big, 16, budget=top64) == _abi.BSA_ERR_UNSUPPORTED
+    msg = L.bsa_last_error().decode()
+    assert str(need) in msg and str(_abi.BSA_STATIC_SCRATCH_BYTES) in msg
