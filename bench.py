@@ -1,36 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark: sparse decode tokens/s and effective HBM bandwidth on one MI355X.
 
-Headline workload: one decode layer shaped like the replay study's model
-(32 q / 4 KV heads, head_dim 128, bf16, 16-token pages) at 29,504 cached tokens
-with a 4096-token budget (top 256 of 1,844 pages), envelope scoring, one
-sequence.  One step = chunk scoring + per-KV-head top-k + split-K sparse
-attention + split merge for the whole batch, run as the library's decode step:
-bsa_score_chunks then bsa_select_attn_decode (selection fused into the
-attention kernel).  The unfused sequence (bsa_select_topk then
-bsa_sparse_attn_decode) is timed beside it.  Chunk metadata is built once
+Headline workload (the metric's own point, 32K context, budget 4096): one
+decode layer shaped like the replay study's model (32 q / 4 KV heads,
+head_dim 128, bf16, 16-token pages) at 32,768 cached tokens, top 256 of 2,048
+pages per KV head (4,096 tokens), envelope scoring, one sequence.  One step =
+chunk scoring + per-KV-head top-k + split-K sparse attention + split merge,
+run as the library's decode step, bsa_decode_step (three launches: scoring,
+the fused selection + attention, the split merge).  The unfused sequence
+(bsa_score_chunks, bsa_select_topk, bsa_sparse_attn_decode) is timed beside
+it.  Chunk metadata is built once
 before timing (in a live loop a page's metadata is written once per 16 decode
-steps) and its build time is reported apart.  Per-kernel figures (the fused
-kernel, the decode kernel and the merge alone) come from HIP events around
-graph replays of that launch alone on its stream (the split partials are left
-in the workspace and merged by a separate call).
+steps) and its build time is reported apart.
 
+Cold cache: every workload rotates over replicas of its K/V cache and
+metadata, as many as make the bytes one rotation touches (metadata + selected
+K/V + scores + q / out, per step) reach 1 GiB, so the 256 MB last-level cache
+cannot serve a step from an earlier one; step and per-kernel timings use the
+same rotation, and every record names touched_bytes and cache_replicas.
 Inputs are synthetic and seeded (block_sparse_attention_chunk_amd/synth.py)
-and resident in HBM before the timed region.  Steps rotate over replicas of
-the cache and metadata whose total exceeds 1 GiB, so the 256 MB last-level
-cache cannot serve the reads.  Each step is captured once in a HIP graph and
-replayed, so host dispatch is not in the measurement.
+and resident in HBM before the timed region.  Steps are captured in HIP graphs
+and replayed, so host dispatch is not in the measurement: exactly --steps
+steps are timed as one graph replay (the headline value), and separately 100
+replays of 16-step graphs (rotating over the replicas) are each timed with HIP
+events for the median and p10 / p90 of the per-step time.  Per-kernel figures come from HIP events around graph replays of that
+launch alone on its stream.
 
-Extra records in the same JSON line: the same layer with 16 sequences at
-32,768 tokens; a 64 q / 8 KV-head batch of 16 x 32,768 tokens at ratio 1/8
-(4096 tokens per sequence and head); the 131,072-token router prefill (28 q /
-4 KV heads, k = 32, rho = 2) with its MFMA utilisation, and the same router
-at 32,768 and 65,536 tokens; a 48-layer decode step (48 replay-shaped layers
-with their own caches, one HIP graph) at 1 and 16 sequences; with --extra
-also every budget against the dense kernel: top-256 / top-512 pages on the
-29,504-token layer with both scorings, token budgets 4096 / 8192 / 16384 over
-variable chunks, and the seven ratios of the 8K-32K batched workload with
-both scorings.
+Records in the same JSON line: the same layer with 16 sequences at 32,768
+tokens; a 64 q / 8 KV-head batch of 16 x 32,768 tokens at ratio 1/8 (4096
+tokens per sequence and head); the ragged 16 x U[8K, 32K] batch at ratio 1/2;
+the speedup over this build's dense kernel at every budget (top-256 / top-512
+pages on the 29,504-token layer with both scorings, token budgets 4096 / 8192
+/ 16384 over variable chunks, and the seven ratios of the ragged batch with
+both scorings); the 131,072-token router prefill (28 q / 4 KV heads, k = 32,
+rho = 2) with its MFMA utilisation, and the same router at 32,768 and 65,536
+tokens; a 48-layer decode step at 1 and 16 sequences; and the fp64 oracle
+timed on the host cores (all threads and one thread; decode steps of the
+headline workload, and the router-prefill stages on a stated subset).
 
 Prints one JSON line.  --gpus N > 1 is refused (one GPU per box).
 """
@@ -60,17 +66,20 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--budget", type=int, default=4096, help="attended tokens per (sequence, KV head)")
     ap.add_argument("--scoring", choices=["envelope", "centroid"], default="envelope")
-    ap.add_argument("--replicas-gib", type=float, default=1.0)
+    ap.add_argument("--seq-len", type=int, default=32768, help="cached tokens of the headline sequence")
+    ap.add_argument("--replicas-gib", type=float, default=1.0,
+                    help="bytes touched per rotation over the cache replicas (cold-cache mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-batched", action="store_true", help="skip the batched extra records")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle decode steps on all host threads")
+    ap.add_argument("--cpu-seconds-1t", type=float, default=5.0, help="oracle decode steps on one thread")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched records")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the every-budget speedup records")
     ap.add_argument("--no-prefill", action="store_true", help="skip the router prefill records")
     ap.add_argument("--no-layers", action="store_true", help="skip the 48-layer decode-step records")
-    ap.add_argument("--extra", action="store_true", help="also the seven-ratio batched sweep")
-    ap.add_argument("--extra-ratios", type=str, default="",
-                    help="comma-separated subset of the sweep's ratios (default: all seven)")
-    ap.add_argument("--only-headline-kernel", action="store_true",
-                    help="profiling aid: time only the headline workload")
+    ap.add_argument("--sweep-ratios", type=str, default="",
+                    help="comma-separated subset of the ragged batch's ratios (default: all seven)")
+    ap.add_argument("--only", choices=["headline", "h1b16", "h2", "ragged"], default=None,
+                    help="profiling aid: run only this decode workload's timing loops and print its record")
     ap.add_argument("--kernel-launches", type=int, default=200, help="launches per per-kernel timing loop")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="profiling aid: after timing, copy this many MiB device-to-device once (a plain copy of "
@@ -82,8 +91,94 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def replicas_for(touched_bytes, gib):
+    """Cache replicas whose rotation touches at least `gib` GiB."""
+    return max(1, math.ceil(gib * 2 ** 30 / max(1, touched_bytes)))
+
+
+def percentiles(samples):
+    x = np.sort(np.asarray(samples))
+    return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)), "p90": float(np.percentile(x, 90)),
+            "n": int(x.size)}
+
+
+class Rotation:
+    """HIP graphs of a workload's step (or kernel) over its cache replicas, and
+    the timing protocols used on them."""
+
+    def __init__(self, torch, dev, replicas):
+        self.torch, self.dev, self.R = torch, dev, replicas
+
+    def graph(self, fn, reps):
+        torch = self.torch
+        for r in sorted(set(reps)):   # code objects are loaded before capture
+            fn(r)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in reps:
+                fn(r)
+        torch.cuda.synchronize()
+        return g
+
+    def time_steps(self, fn, steps, warmup):
+        """Exactly `steps` calls of fn, rotating replicas, timed as one replay
+        of a graph that holds all of them (after a graph of `warmup` calls on
+        the replicas before them), so no host dispatch falls between steps;
+        mean time per call."""
+        torch, R = self.torch, self.R
+        g_warm = self.graph(fn, [r % R for r in range(warmup)]) if warmup else None
+        g_steps = self.graph(fn, [(warmup + i) % R for i in range(steps)])
+        if g_warm is not None:
+            g_warm.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g_steps.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def sample_steps(self, fn, n, block=16):
+        """At least n per-call samples: graphs of `block` consecutive calls
+        covering the replicas in rotation are replayed in turn, each replay
+        bracketed by HIP events on the launch stream; a sample is the mean
+        call time of one replay (single-call replays would measure the host's
+        graph launch, not the device, for calls of a few microseconds)."""
+        torch, R = self.torch, self.R
+        n_graphs = max(1, math.ceil(R / block))
+        graphs = [self.graph(fn, [(block * j + i) % R for i in range(block)]) for j in range(n_graphs)]
+        stream = torch.cuda.current_stream(self.dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for g in graphs:
+            g.replay()
+        for i in range(n):
+            ev[i][0].record(stream)
+            graphs[i % n_graphs].replay()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e-3 / block for a, b in ev]
+
+    def time_kernel(self, fn, min_launches=200):
+        """Average duration of one launch of fn: back-to-back launches over the
+        replicas (at least 32 per graph), bracketed by HIP events on the launch
+        stream."""
+        torch, R = self.torch, self.R
+        reps = list(range(R)) * max(1, math.ceil(32 / R))
+        per = max(1, math.ceil(min_launches / len(reps)))
+        g = self.graph(fn, reps)
+        stream = torch.cuda.current_stream(self.dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        e0.record(stream)
+        for _ in range(per):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (per * len(reps))
+
+
 class DecodeBench:
-    """Device buffers, graphs and timings of one decode workload."""
+    """Device buffers, graphs and timings of one decode workload on 16-token
+    pages, rotating over cold cache replicas."""
 
     def __init__(self, case, budget, scoring, dev, replicas_gib=1.0):
         import torch
@@ -92,12 +187,16 @@ class DecodeBench:
         self.scoring = scoring
         self.kind = ops.BSA_ENVELOPE if scoring == "envelope" else ops.BSA_CENTROID
         self.budget = budget
+        self.which = ops.BSA_META_ENVELOPE if self.kind == ops.BSA_ENVELOPE else ops.BSA_META_CENTROID
+        B, H = case.batch, case.num_kv_heads
+        max_pages = int(case.block_table.shape[1])
+        meta_b, kv_b, qo_b, _ = self.bytes()
+        self.touched = meta_b + kv_b + qo_b + B * H * max_pages * 4   # + the score row written and read
+        self.replicas = replicas_for(self.touched, replicas_gib)
+        self.rot = Rotation(torch, dev, self.replicas)
         base_k, base_v = ops.upload(case.k, dev), ops.upload(case.v, dev)
         self.q = ops.upload(case.q, dev)
         bt, sl = ops.upload(case.block_table, dev), ops.upload(case.seq_lens, dev)
-        self.which = ops.BSA_META_ENVELOPE if self.kind == ops.BSA_ENVELOPE else ops.BSA_META_CENTROID
-        kv_bytes = case.k.nbytes + case.v.nbytes
-        self.replicas = max(1, math.ceil(replicas_gib * 2 ** 30 / kv_bytes))
         self.reps = []
         for r in range(self.replicas):
             k = base_k if r == 0 else base_k.clone()
@@ -106,10 +205,9 @@ class DecodeBench:
             self.reps.append((kv, ops.build_chunk_meta(kv, which=self.which)))
         kv0 = self.reps[0][0]
         self.max_sel = budget.max_selected(kv0.max_pages)
-        B, H = case.batch, case.num_kv_heads
         self.scores = torch.empty((B, H, kv0.max_pages), dtype=torch.float32, device=dev)
-        self.sel = torch.empty((B, H, self.max_sel), dtype=torch.int32, device=dev)
-        self.cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+        self.sel = torch.full((B, H, self.max_sel), -1, dtype=torch.int32, device=dev)
+        self.cnt = torch.zeros((B, H), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
         self.ws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, self.max_sel), 1),),
                               dtype=torch.uint8, device=dev)
@@ -122,6 +220,8 @@ class DecodeBench:
         self.dws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, kv0.max_pages,
                                                                self.dense_candidates[-1]), 1),),
                                dtype=torch.uint8, device=dev)
+        self.sws = torch.empty((ops.decode_step_workspace_bytes(kv0, case.num_q_heads, budget),), dtype=torch.uint8,
+                               device=dev)
 
     # --- the hot path ---------------------------------------------------------------
     def score(self, r):
@@ -159,9 +259,10 @@ class DecodeBench:
         return self.ops.PARTIALS if self.splits > 1 else self.out
 
     def step(self, r):
-        """The decode step: scores, then selection + attention + merge."""
-        self.score(r)
-        self.fused(r)
+        """The decode step, bsa_decode_step: scoring, then the fused selection
+        + attention, then the split merge."""
+        kv, meta = self.reps[r]
+        self.ops.decode_step(self.q, kv, meta, self.kind, self.budget, out=self.out, workspace=self.sws)
 
     def step_unfused(self, r):
         self.select(r)
@@ -177,7 +278,7 @@ class DecodeBench:
         best = None
         for s in self.dense_candidates:
             self.dense_splits = s
-            t = self.time_kernel(self.dense, launches)
+            t = self.rot.time_kernel(self.dense, launches)
             if best is None or t < best[0]:
                 best = (t, s)
         self.dense_splits = best[1]
@@ -186,64 +287,6 @@ class DecodeBench:
     def meta(self, r):
         kv, meta = self.reps[r]
         self.ops.build_chunk_meta(kv, which=self.which, meta=meta)
-
-    # --- graphs and timing ----------------------------------------------------------
-    def graph(self, fn, reps):
-        torch = self.torch
-        for r in reps:   # code objects are loaded before capture
-            fn(r)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in reps:
-                fn(r)
-        torch.cuda.synchronize()
-        return g
-
-    def time_steps(self, steps, warmup, fn=None):
-        """Exactly `steps` decode steps, rotating replicas, from HIP graphs.  A
-        graph holds whole rounds over the replicas, at least 16 steps, so the
-        replay's host overhead stays hidden behind the device work."""
-        torch = self.torch
-        fn = fn or self.step
-        R = self.replicas
-        rounds = max(1, math.ceil(16 / R))
-        g_block = self.graph(fn, list(range(R)) * rounds)
-        g_one = [self.graph(fn, [r]) for r in range(R)]
-        per_block = R * rounds
-
-        def run(n):
-            full, rem = divmod(n, per_block)
-            for _ in range(full):
-                g_block.replay()
-            for r in range(rem):
-                g_one[r % R].replay()
-
-        run(warmup)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run(steps)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
-
-    def time_kernel(self, fn, min_launches=200):
-        """Average duration of one launch of fn: back-to-back launches over the
-        replicas (at least 32 per graph), bracketed by HIP events on the launch
-        stream."""
-        torch = self.torch
-        R = self.replicas
-        reps = list(range(R)) * max(1, math.ceil(32 / R))
-        per = max(1, math.ceil(min_launches / len(reps)))
-        g = self.graph(fn, reps)
-        stream = torch.cuda.current_stream(self.dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g.replay()
-        e0.record(stream)
-        for _ in range(per):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / (per * len(reps))
 
     def bytes(self):
         """Algorithmic bytes of one step: metadata read + selected K/V + q in + out."""
@@ -264,22 +307,38 @@ class DecodeBench:
         qo = B * Hq * D * (2 + 4)
         return meta, kvb, qo, dense_kv
 
-    def measure(self, steps, warmup, launches=200):
-        t_step = self.time_steps(steps, warmup)
-        t_step_unfused = self.time_steps(steps, warmup, self.step_unfused)
+    def measure(self, steps, warmup, launches=200, samples=100):
+        rot = self.rot
+        t_step = rot.time_steps(self.step, steps, warmup)
+        pct = percentiles(rot.sample_steps(self.step, max(samples, steps)))
+        t_step_unfused = rot.time_steps(self.step_unfused, steps, warmup)
         self.step_unfused(0)
         self.torch.cuda.synchronize()
-        m = {"t_step": t_step, "t_step_unfused": t_step_unfused,
-             "t_fused": self.time_kernel(self.fused, launches),
-             "t_fused_kernel": self.time_kernel(self.fused_kernel, launches),
-             "t_attn": self.time_kernel(self.attend, launches),
-             "t_decode_kernel": self.time_kernel(self.decode_kernel, launches),
+        m = {"t_step": t_step, "step_pct": pct, "t_step_unfused": t_step_unfused,
+             "t_fused": rot.time_kernel(self.fused, launches),
+             "t_fused_kernel": rot.time_kernel(self.fused_kernel, launches),
+             "t_attn": rot.time_kernel(self.attend, launches),
+             "t_decode_kernel": rot.time_kernel(self.decode_kernel, launches),
              "t_dense": self.time_dense(launches),
-             "t_score": self.time_kernel(self.score, launches),
-             "t_select": self.time_kernel(self.select, launches),
-             "t_meta": self.time_kernel(self.meta, launches)}
+             "t_score": rot.time_kernel(self.score, launches),
+             "t_select": rot.time_kernel(self.select, launches),
+             "t_meta": rot.time_kernel(self.meta, launches)}
         self.decode_kernel(0)
-        m["t_merge"] = self.time_kernel(self.merge, launches) if self.splits > 1 else 0.0
+        m["t_merge"] = rot.time_kernel(self.merge, launches) if self.splits > 1 else 0.0
+        meta_b, kv_b, qo_b, dense_b = self.bytes()
+        m.update({"meta_bytes": meta_b, "kv_bytes": kv_b, "qo_bytes": qo_b, "dense_kv_bytes": dense_b})
+        return m
+
+    def measure_light(self, steps, warmup, launches=64, t_dense=None):
+        """Step, attention call and dense attention only (the budget sweep)."""
+        rot = self.rot
+        t_step = rot.time_steps(self.step, steps, warmup)
+        self.select(0)          # the attention calls below read this selection
+        self.torch.cuda.synchronize()
+        m = {"t_step": t_step,
+             "t_attn": rot.time_kernel(self.attend, launches),
+             "t_decode_kernel": rot.time_kernel(self.decode_kernel, launches),
+             "t_dense": t_dense if t_dense is not None else self.time_dense(launches)}
         meta_b, kv_b, qo_b, dense_b = self.bytes()
         m.update({"meta_bytes": meta_b, "kv_bytes": kv_b, "qo_bytes": qo_b, "dense_kv_bytes": dense_b})
         return m
@@ -289,12 +348,15 @@ def record(name, bench, m):
     case = bench.case
     step_bytes = m["meta_bytes"] + m["kv_bytes"] + m["qo_bytes"]
     kvb = m["kv_bytes"]
+    pct = m["step_pct"]
     return {
         "workload": name,
         "batch": case.batch, "seq_len": int(case.seq_lens.max()), "q_heads": case.num_q_heads,
         "kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "scoring": bench.scoring,
         "tokens_per_s": case.batch / m["t_step"],
         "us_per_step": m["t_step"] * 1e6,
+        "us_per_step_median": pct["median"] * 1e6, "us_per_step_p10": pct["p10"] * 1e6,
+        "us_per_step_p90": pct["p90"] * 1e6, "step_samples": pct["n"], "steps_per_sample": 16,
         "unfused_us_per_step": m["t_step_unfused"] * 1e6,
         "effective_hbm_gbs": step_bytes / m["t_step"] / 1e9,
         "effective_hbm_frac": step_bytes / m["t_step"] / 1e9 / HBM_PEAK_GBS,
@@ -315,11 +377,24 @@ def record(name, bench, m):
         "dense_kv_gbs": m["dense_kv_bytes"] / m["t_dense"] / 1e9,
         "speedup_attn_vs_dense": m["t_dense"] / m["t_attn"],
         "speedup_step_vs_dense": m["t_dense"] / m["t_step"],
+        "step_over_dense": m["t_step"] / m["t_dense"],
         "splits": bench.splits,
         "dense_splits": bench.dense_splits,
         "cache_replicas": bench.replicas,
+        "touched_bytes": bench.touched,
         "bytes_per_step": {"metadata": m["meta_bytes"], "selected_kv": kvb, "q_out": m["qo_bytes"]},
     }
+
+
+def record_light(name, bench, m, budget):
+    kvb = m["kv_bytes"]
+    return {"workload": name, "budget": budget, "us_per_step": m["t_step"] * 1e6,
+            "tokens_per_s": bench.case.batch / m["t_step"], "sparse_attn_us": m["t_attn"] * 1e6,
+            "decode_kernel_us": m["t_decode_kernel"] * 1e6, "dense_attn_us": m["t_dense"] * 1e6,
+            "speedup_attn_vs_dense": m["t_dense"] / m["t_attn"], "speedup_step_vs_dense": m["t_dense"] / m["t_step"],
+            "attn_selected_kv_gbs": kvb / m["t_attn"] / 1e9, "selected_kv_gbs": kvb / m["t_decode_kernel"] / 1e9,
+            "selected_kv_frac": kvb / m["t_decode_kernel"] / 1e9 / HBM_PEAK_GBS,
+            "cache_replicas": bench.replicas, "touched_bytes": bench.touched}
 
 
 class ChunkedDecodeBench(DecodeBench):
@@ -335,10 +410,16 @@ class ChunkedDecodeBench(DecodeBench):
         self.scoring, self.kind, self.budget = "envelope", ops.BSA_ENVELOPE, budget
         self.which = ops.BSA_META_ENVELOPE
         self.chunks = ops.Chunks(ops.upload(case.chunk_starts, dev), ops.upload(case.num_chunks, dev))
+        B, H, D = case.batch, case.num_kv_heads, case.head_dim
+        mc = self.chunks.max_chunks
+        # touched per step: metadata, at most the budget of K/V per head, scores, q / out
+        self.touched = (int(case.num_chunks.sum()) * H * 2 * D * 2 + B * H * min(budget.tokens, int(case.seq_lens.max()))
+                        * D * 2 * 2 + B * H * mc * 4 + B * case.num_q_heads * D * 6)
+        self.replicas = replicas_for(self.touched, replicas_gib)
+        self.rot = Rotation(torch, dev, self.replicas)
         base_k, base_v = ops.upload(case.k, dev), ops.upload(case.v, dev)
         self.q = ops.upload(case.q, dev)
         bt, sl = ops.upload(case.block_table, dev), ops.upload(case.seq_lens, dev)
-        self.replicas = max(1, math.ceil(replicas_gib * 2 ** 30 / (case.k.nbytes + case.v.nbytes)))
         self.reps = []
         for r in range(self.replicas):
             k = base_k if r == 0 else base_k.clone()
@@ -346,12 +427,10 @@ class ChunkedDecodeBench(DecodeBench):
             kv = ops.KVCache(k, v, sl, case.page_size, bt)
             self.reps.append((kv, ops.build_chunk_meta(kv, self.chunks, which=self.which)))
         kv0 = self.reps[0][0]
-        mc = self.chunks.max_chunks
         self.max_sel = budget.max_selected(mc)
-        B, H = case.batch, case.num_kv_heads
         self.scores = torch.empty((B, H, mc), dtype=torch.float32, device=dev)
-        self.sel = torch.empty((B, H, self.max_sel), dtype=torch.int32, device=dev)
-        self.cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+        self.sel = torch.full((B, H, self.max_sel), -1, dtype=torch.int32, device=dev)
+        self.cnt = torch.zeros((B, H), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
         self.ws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, self.max_sel), 1),),
                               dtype=torch.uint8, device=dev)
@@ -382,8 +461,9 @@ class ChunkedDecodeBench(DecodeBench):
         self.select(r)
         self.attend(r)
 
-    def measure(self, steps, warmup, launches=200):
-        t_step = self.time_steps(steps, warmup)
+    def measure(self, steps, warmup, launches=64):
+        rot = self.rot
+        t_step = rot.time_steps(self.step, steps, warmup)
         self.select(0)
         self.torch.cuda.synchronize()
         case, D, H = self.case, self.case.head_dim, self.case.num_kv_heads
@@ -392,16 +472,17 @@ class ChunkedDecodeBench(DecodeBench):
                    for b in range(case.batch) for h in range(H))
         kv_b = kept * D * 2 * 2
         meta_b = int(case.num_chunks.sum()) * H * 2 * D * 2
-        t_attn, t_dense = self.time_kernel(self.attend, launches), self.time_kernel(self.dense, launches)
+        t_attn, t_dense = rot.time_kernel(self.attend, launches), rot.time_kernel(self.dense, launches)
         return {"workload": f"variable chunks (U[16,256] tokens, {int(case.num_chunks.max())} chunks), "
                             f"1 x {int(case.seq_lens.max())} tokens, envelope, token budget {self.budget.tokens}",
-                "budget_tokens": self.budget.tokens, "attended_tokens_per_head": kept / (case.batch * H),
+                "budget": f"{self.budget.tokens} tokens", "attended_tokens_per_head": kept / (case.batch * H),
                 "tokens_per_s": case.batch / t_step, "us_per_step": t_step * 1e6,
-                "score_select_us": self.time_kernel(self.select, launches) * 1e6,
+                "score_select_us": rot.time_kernel(self.select, launches) * 1e6,
                 "sparse_attn_us": t_attn * 1e6, "dense_attn_us": t_dense * 1e6,
-                "selected_kv_gbs": kv_b / t_attn / 1e9,
+                "attn_selected_kv_gbs": kv_b / t_attn / 1e9,
                 "effective_hbm_gbs": (meta_b + kv_b) / t_step / 1e9,
-                "speedup_attn_vs_dense": t_dense / t_attn, "speedup_step_vs_dense": t_dense / t_step}
+                "speedup_attn_vs_dense": t_dense / t_attn, "speedup_step_vs_dense": t_dense / t_step,
+                "cache_replicas": self.replicas, "touched_bytes": self.touched}
 
 
 class PrefillBench:
@@ -503,8 +584,7 @@ class PrefillBench:
 class LayerStackBench:
     """A serving-shaped decode step: `layers` replay-shaped layers, each with
     its own K/V cache and metadata (device copies of one generated layer),
-    every layer running scoring + fused selection / attention + merge; the
-    whole step is one HIP graph."""
+    every layer running bsa_decode_step; the whole step is one HIP graph."""
 
     def __init__(self, case, budget, scoring, dev, layers=48):
         import torch
@@ -524,8 +604,7 @@ class LayerStackBench:
         B, H = case.batch, case.num_kv_heads
         self.scores = torch.empty((B, H, kv0.max_pages), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
-        K = budget.max_selected(kv0.max_pages)
-        self.ws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, K), 1),), dtype=torch.uint8,
+        self.ws = torch.empty((ops.decode_step_workspace_bytes(kv0, case.num_q_heads, budget),), dtype=torch.uint8,
                               device=dev)
         self.dws = torch.zeros((max(ops.decode_workspace_bytes(kv0, case.num_q_heads, kv0.max_pages), 1),),
                                dtype=torch.uint8, device=dev)
@@ -533,8 +612,7 @@ class LayerStackBench:
     def step(self):
         ops = self.ops
         for kv, meta in self.stack:
-            ops.score_chunks(self.q, kv, meta, self.kind, out=self.scores)
-            ops.select_attn_decode(self.q, kv, self.scores, self.budget, out=self.out, workspace=self.ws)
+            ops.decode_step(self.q, kv, meta, self.kind, self.budget, out=self.out, workspace=self.ws)
 
     def dense_step(self):
         for kv, _ in self.stack:
@@ -568,7 +646,7 @@ class LayerStackBench:
                 "speedup_vs_dense_attention": res["dense"] / res["sparse"]}
 
 
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_decode_replay_b1_hbm_traffic.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_decode_replay_32k_b1_hbm_traffic.txt")
 KERNEL_SOURCES = ["select_decode.hip", "decode_common.h", "radix_select.h", "select_rules.h", "bsa_internal.h"]
 
 
@@ -598,14 +676,17 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(case, k_pages, scoring, seconds):
-    """The fp64 oracle on the host cores on the same inputs and stages (score +
-    select + attention per step, metadata built once), run for ~`seconds`."""
-    import oracle
-    oc = oracle.PagedCache(case.k, case.v, case.block_table, case.seq_lens, case.page_size, case.num_kv_heads,
-                           case.head_dim)
-    meta = oracle.chunk_meta(oc)
-    kind = oracle.ENVELOPE if scoring == "envelope" else oracle.CENTROID
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_decode_rate(oracle, case, oc, meta, kind, k_pages, seconds):
     n = case.n_chunks()
     steps, t0 = 0, time.perf_counter()
     while True:
@@ -615,11 +696,157 @@ def cpu_baseline(case, k_pages, scoring, seconds):
         steps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": case.batch * steps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} complete decode steps of the headline workload (score + select + attention over "
-                      f"the same inputs; metadata built once) in {el:.1f} s, fp64, OpenMP {threads} threads"}
+            return steps, el
+
+
+def cpu_baseline(case, k_pages, scoring, seconds, seconds_1t, prefill_blocks=None):
+    """The fp64 oracle on the host cores on the same inputs and stages as the
+    headline step (score + select + attention per step, metadata built once),
+    with every thread the process may use and with one thread; then the
+    router-prefill stages on a stated subset, extrapolated to the full
+    131,072-token prefill."""
+    import oracle
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    used = oracle.max_threads()
+    oc = oracle.PagedCache(case.k, case.v, case.block_table, case.seq_lens, case.page_size, case.num_kv_heads,
+                           case.head_dim)
+    meta = oracle.chunk_meta(oc)
+    kind = oracle.ENVELOPE if scoring == "envelope" else oracle.CENTROID
+    steps, el = _oracle_decode_rate(oracle, case, oc, meta, kind, k_pages, seconds)
+    oracle.set_threads(1)
+    steps1, el1 = _oracle_decode_rate(oracle, case, oc, meta, kind, k_pages, seconds_1t)
+    oracle.set_threads(used)
+    res = {"value": case.batch * steps / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{steps} complete decode steps of the headline workload ({int(case.seq_lens[0])} tokens, "
+                     f"top-{k_pages} pages; score + select + attention over the same inputs, metadata built once) "
+                     f"in {el:.1f} s, fp64, OpenMP {used} threads",
+           "single_thread": {"value": case.batch * steps1 / el1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"{steps1} decode steps in {el1:.1f} s, one thread"}}
+    if prefill_blocks is not None:
+        res["prefill"] = cpu_prefill_stages(oracle, used, prefill_blocks)
+    return res
+
+
+def cpu_prefill_stages(oracle, threads, attended_blocks):
+    """Router-prefill stages of the oracle on a subset of the 131,072-token
+    workload: tile scores of 6 tiles spread over the sequence (cost per tile
+    grows with its visible blocks, t + 1), the router at full size (2,048
+    tiles x 4 heads x 2,048 blocks of seeded scores), and the tile attention
+    of 16 rows over 32 blocks each; each extrapolated by its work unit to the
+    full prefill (attention: the GPU run's attended (tile, KV head, block)
+    count)."""
+    from block_sparse_attention_chunk_amd import synth
+    pc = synth.router_prefill()
+    T, Hq, H, D = pc.T, pc.num_q_heads, pc.num_kv_heads, pc.head_dim
+    nt = T // 64
+    g = Hq // H
+    c = oracle.PagedCache(pc.k, pc.v, None, [T], 64, H, D, strides=(64 * H * D, D, H * D), max_pages=nt)
+    t0 = time.perf_counter()
+    meta = oracle.chunk_meta(c)
+    t_meta = time.perf_counter() - t0
+    tiles = np.array([100, 500, 900, 1300, 1700, 2047])
+    t0 = time.perf_counter()
+    oracle.tile_scores(pc.q, meta, oracle.ENVELOPE, num_kv_heads=H, tile_rows=64, block_size=64, tiles=tiles)
+    t_ts = time.perf_counter() - t0
+    vis_sub = float(np.sum(tiles + 1))
+    vis_all = float(nt * (nt + 1) / 2)
+    rng = np.random.default_rng(4)
+    ts = rng.standard_normal((nt, H, nt))
+    t0 = time.perf_counter()
+    oracle.router(ts, np.arange(nt) + 1, 32, 2)
+    t_router = time.perf_counter() - t0
+    rows = np.array([64 * t + 17 for t in (40, 300, 700, 1100, 1500, 1900, 2047)] +
+                    [64 * t + 63 for t in (60, 400, 800, 1200, 1600, 2000, 2046, 2047, 1000)])
+    kv_idx = np.full((nt, H, 64), -1, np.int32)
+    for t in np.unique(rows // 64):
+        kv_idx[t, :, :32] = np.sort(rng.choice(t + 1, size=32, replace=False))[None, :]
+    t0 = time.perf_counter()
+    oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=H, block_size=64, tile_rows=64, kv_idx=kv_idx, rows=rows)
+    t_attn = time.perf_counter() - t0
+    # attention work unit: (row, q head, block); the sample does rows x Hq x 32
+    per_unit = t_attn / (len(rows) * Hq * 32)
+    full_units = attended_blocks * 64 * g                       # rows per tile x q heads per KV head
+    ext = {"tile_scores_s": t_ts * vis_all / vis_sub, "router_s": t_router, "tile_attn_s": per_unit * full_units,
+           "meta_s": t_meta}
+    total = ext["tile_scores_s"] + ext["router_s"] + ext["tile_attn_s"]
+    return {"value": T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"tile scores of tiles {tiles.tolist()} ({t_ts:.2f} s, x {vis_all / vis_sub:.0f} by visible "
+                      f"blocks), the router over 2048 x 4 x 2048 seeded scores ({t_router:.2f} s), tile attention "
+                      f"of {len(rows)} rows over 32 blocks ({t_attn:.2f} s, extrapolated per (row, q head, block) to "
+                      f"{attended_blocks} attended (tile, KV head, block) triples), metadata ({t_meta:.2f} s, not in "
+                      f"the total); OpenMP {threads} threads",
+            "extrapolated_s": ext, "total_s": total}
+
+
+def decode_workloads(seq_len, budget_tokens, scoring):
+    """(key, label, case, budget, scoring) of the decode records."""
+    from block_sparse_attention_chunk_amd import ops, synth
+    k_pages = budget_tokens // 16
+    yield ("headline", f"replay-shaped decode, 32 q / 4 KV heads, d 128, bf16, {seq_len} tokens, {scoring} scoring, "
+                       f"top-{k_pages} of {(seq_len + 15) // 16} 16-token pages (budget {k_pages * 16} tokens), "
+                       f"1 sequence", lambda: synth.replay_decode(seq_len=seq_len), ops.Budget.topk(k_pages), scoring)
+    yield ("h1b16", "replay-shaped decode, 16 x 32768 tokens, envelope, top-256 pages (4096 tokens)",
+           lambda: synth.replay_decode(seq_len=32768, batch=16), ops.Budget.topk(256), "envelope")
+    yield ("h2", "batched decode, 64 q / 8 KV heads, 16 x 32768 tokens, centroid, ratio 1/8 with bos+eos (4096 "
+                 "tokens per sequence and head)",
+           lambda: synth.batched_decode(cid=3, seq_lens=[32768] * 16), ops.Budget.ratio_budget(0.125, 1, 1),
+           "centroid")
+    yield ("ragged", "batched decode, 64 q / 8 KV heads, 16 x U[8192, 32768] tokens (8,409-30,271), centroid, "
+                     "ratio 1/2 with bos+eos",
+           lambda: synth.batched_decode(), ops.Budget.ratio_budget(0.5, 1, 1), "centroid")
+
+
+def budget_sweep(a, dev):
+    """Speedup over this build's dense kernel at every budget the pages use."""
+    import torch
+    from block_sparse_attention_chunk_amd import ops, synth
+    out = []
+    log("budget sweep: replay-shaped layer, 1 x 29504 tokens, top-256 / top-512, both scorings")
+    c1 = synth.replay_decode()
+    t_dense = None
+    for scoring in ("envelope", "centroid"):
+        for k in (256, 512):
+            log(f"  {scoring} top-{k}")
+            b = DecodeBench(c1, ops.Budget.topk(k), scoring, dev, a.replicas_gib)
+            m = b.measure_light(60, 5, t_dense=t_dense)
+            t_dense = m["t_dense"]
+            out.append(record_light(f"replay-shaped decode, 1 x 29504 tokens, {scoring}, top-{k} pages", b, m,
+                                    f"{16 * k} tokens"))
+            del b
+            torch.cuda.empty_cache()
+    del c1
+    log("budget sweep: variable chunks, 1 x 29504 tokens, token budgets 4096 / 8192 / 16384")
+    c2 = synth.varchunk_decode()
+    for tokens in (4096, 8192, 16384):
+        log(f"  {tokens} tokens")
+        b = ChunkedDecodeBench(c2, ops.Budget.token_budget(tokens), dev, a.replicas_gib)
+        out.append(b.measure(60, 5))
+        del b
+        torch.cuda.empty_cache()
+    del c2
+    c2b = synth.varchunk_decode(seq_len=16384)
+    b = ChunkedDecodeBench(c2b, ops.Budget.token_budget(16384), dev, a.replicas_gib)
+    out.append(b.measure(60, 5))
+    del b, c2b
+    torch.cuda.empty_cache()
+    log("budget sweep: 16 x U[8K, 32K] tokens, 64 q / 8 KV heads, seven ratios, both scorings")
+    c3 = synth.batched_decode()
+    ratios = [float(x) for x in a.sweep_ratios.split(",")] if a.sweep_ratios else synth.RATIOS
+    t_dense = None
+    for scoring, bos in (("centroid", 1), ("envelope", 0)):
+        for ratio in ratios:
+            log(f"  {scoring} ratio {ratio}")
+            b = DecodeBench(c3, ops.Budget.ratio_budget(ratio, bos, 1), scoring, dev, a.replicas_gib)
+            m = b.measure_light(30, 3, t_dense=t_dense)
+            t_dense = m["t_dense"]
+            out.append(record_light(f"batched decode, 16 x U[8K, 32K], {scoring} (bos={bos}, eos=1), ratio {ratio}",
+                                    b, m, f"ratio {ratio}"))
+            del b
+            torch.cuda.empty_cache()
+    del c3
+    return out
 
 
 def main():
@@ -631,14 +858,28 @@ def main():
     from block_sparse_attention_chunk_amd import ops, synth
     dev = torch.device("cuda:0")
 
-    log("headline: replay-shaped decode layer")
-    case = synth.replay_decode()
-    k_pages = a.budget // case.page_size
-    hb = DecodeBench(case, ops.Budget.topk(k_pages), a.scoring, dev, a.replicas_gib)
-    m = hb.measure(a.steps, a.warmup, a.kernel_launches)
-    head = record(f"replay-shaped decode, {case.num_q_heads} q / {case.num_kv_heads} KV heads, d 128, bf16, "
-                  f"{int(case.seq_lens[0])} tokens, {a.scoring} scoring, top-{k_pages} of "
-                  f"{int(case.n_chunks()[0])} 16-token pages (budget {k_pages * 16} tokens), 1 sequence", hb, m)
+    recs = {}
+    head_case = None
+    for key, label, make, budget, scoring in decode_workloads(a.seq_len, a.budget, a.scoring):
+        if a.only and key != a.only:
+            continue
+        if key != "headline" and (a.no_batched and not a.only):
+            continue
+        log(f"decode: {label}")
+        case = make()
+        b = DecodeBench(case, budget, scoring, dev, a.replicas_gib)
+        steps = a.steps if key == "headline" else max(50, a.steps // 4)
+        m = b.measure(steps, a.warmup if key == "headline" else 5, a.kernel_launches)
+        recs[key] = (record(label, b, m), m)
+        if key == "headline":
+            head_case = case
+        del b
+        torch.cuda.empty_cache()
+
+    if a.only:
+        print(json.dumps(recs[a.only][0]), flush=True)
+        return
+    head, m = recs["headline"]
     res = {
         "metric": "sparse decode tokens/s + effective HBM GB/s (% of peak) at 32K ctx, budget 4096",
         "value": head["tokens_per_s"],
@@ -652,53 +893,35 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) keys/values, 24 planted needle pages, 4 outlier channels x8",
-        "config": {"workload": head["workload"], "batch": 1, "seq_len": int(case.seq_lens[0]),
-                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
-                   "page_size": case.page_size, "budget_tokens": k_pages * 16, "scoring": a.scoring,
-                   "splits": hb.splits, "cache_replicas": hb.replicas, "graph_replay": True},
+        "config": {"workload": head["workload"], "batch": 1, "seq_len": int(head_case.seq_lens[0]),
+                   "q_heads": head_case.num_q_heads, "kv_heads": head_case.num_kv_heads,
+                   "head_dim": head_case.head_dim, "page_size": head_case.page_size, "budget_tokens": a.budget,
+                   "scoring": a.scoring, "splits": head["splits"], "cache_replicas": head["cache_replicas"],
+                   "touched_bytes": head["touched_bytes"], "graph_replay": True},
         "effective_hbm_gbs": head["effective_hbm_gbs"],
         "effective_hbm_frac": head["effective_hbm_frac"],
+        "us_per_step_median": head["us_per_step_median"],
+        "us_per_step_p10": head["us_per_step_p10"],
+        "us_per_step_p90": head["us_per_step_p90"],
         "roofline": {"bound": "hbm",
-                     "kernel": "select_decode_kernel (bsa_select_attn_decode without the merge)",
+                     "kernel": "select_decode_kernel (the fused selection + attention launch of the step)",
                      "achieved": head["fused_kernel_selected_kv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["fused_kernel_selected_kv_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": m["kv_bytes"],
                      "launch_us": m["t_fused_kernel"] * 1e6},
         "headline": head,
     }
-    del hb
-    torch.cuda.empty_cache()
-
-    if not a.no_batched and not a.only_headline_kernel:
-        extra = []
-        log("batched: replay-shaped layer, 16 sequences x 32768 tokens")
-        c16 = synth.replay_decode(seq_len=32768, batch=16)
-        b16 = DecodeBench(c16, ops.Budget.topk(256), "envelope", dev, a.replicas_gib)
-        extra.append(record("replay-shaped decode, 16 x 32768 tokens, envelope, top-256 pages (4096 tokens)", b16,
-                            b16.measure(max(50, a.steps // 4), 5)))
-        del b16, c16
-        torch.cuda.empty_cache()
-        log("batched: 64 q / 8 KV heads, 16 x 32768 tokens, ratio 1/8")
-        c3 = synth.batched_decode(cid=3, seq_lens=[32768] * 16)
-        b3 = DecodeBench(c3, ops.Budget.ratio_budget(0.125, 1, 1), "centroid", dev, a.replicas_gib)
-        extra.append(record("batched decode, 64 q / 8 KV heads, 16 x 32768 tokens, centroid, ratio 1/8 with "
-                            "bos+eos (4096 tokens per sequence and head)", b3, b3.measure(max(50, a.steps // 4), 5)))
-        del b3, c3
-        torch.cuda.empty_cache()
-        log("batched: 64 q / 8 KV heads, 16 x U[8K, 32K] tokens, ratio 1/2")
-        cr = synth.batched_decode()
-        br = DecodeBench(cr, ops.Budget.ratio_budget(0.5, 1, 1), "centroid", dev, a.replicas_gib)
-        extra.append(record("batched decode, 64 q / 8 KV heads, 16 x U[8192, 32768] tokens (8,409-30,271), centroid, "
-                            "ratio 1/2 with bos+eos; attention call on the balanced schedule", br,
-                            br.measure(max(50, a.steps // 4), 5)))
-        del br, cr
-        torch.cuda.empty_cache()
-        res["batched"] = extra
-    if not a.no_prefill and not a.only_headline_kernel:
+    if not a.no_batched:
+        res["batched"] = [recs[k][0] for k in ("h1b16", "h2", "ragged")]
+    if not a.no_sweep:
+        res["budget_sweep"] = budget_sweep(a, dev)
+    attended = None
+    if not a.no_prefill:
         log("router prefill: 131072 tokens")
         pc = synth.router_prefill()
         pb = PrefillBench(pc, dev, ops.BSA_ENVELOPE)
         res["prefill"] = pb.measure()
+        attended = res["prefill"]["attended_blocks"]
         del pb, pc
         torch.cuda.empty_cache()
         by_len = []
@@ -706,62 +929,23 @@ def main():
             log(f"router prefill: {T} tokens")
             pc = synth.router_prefill(T=T, groups=max(4, T // 8192), tied_groups=tuple(range(3, max(4, T // 8192), 4)))
             pb = PrefillBench(pc, dev, ops.BSA_ENVELOPE)
-            m = pb.measure()
-            by_len.append({k: m[k] for k in ("workload", "tokens_per_s", "sparse_pipeline_ms", "tile_score_ms",
-                                             "router_ms", "sparse_attn_ms", "dense_causal_attn_ms",
-                                             "sparse_pipeline_vs_dense_attn", "triggered_tiles", "attn_mfma_frac")})
+            mm = pb.measure()
+            by_len.append({k: mm[k] for k in ("workload", "tokens_per_s", "sparse_pipeline_ms", "tile_score_ms",
+                                              "router_ms", "sparse_attn_ms", "dense_causal_attn_ms",
+                                              "sparse_pipeline_vs_dense_attn", "triggered_tiles", "attn_mfma_frac")})
             del pb, pc
             torch.cuda.empty_cache()
         res["prefill_by_length"] = by_len
-    if not a.no_layers and not a.only_headline_kernel:
+    if not a.no_layers:
         stacks = []
-        for B, L in ((1, None), (16, 32768)):
+        for B, L in ((1, 32768), (16, 32768)):
             log(f"48-layer decode step, {B} sequence(s)")
-            c = synth.replay_decode() if L is None else synth.replay_decode(seq_len=L, batch=B)
+            c = synth.replay_decode(seq_len=L) if B == 1 else synth.replay_decode(seq_len=L, batch=B)
             lb = LayerStackBench(c, ops.Budget.topk(256), "envelope", dev)
             stacks.append(lb.measure())
             del lb, c
             torch.cuda.empty_cache()
         res["layer_stack"] = stacks
-    if a.extra:
-        keep = ("workload", "tokens_per_s", "us_per_step", "unfused_us_per_step", "sparse_attn_us", "attn_selected_kv_gbs",
-                "selected_kv_gbs", "selected_kv_frac",
-                "dense_attn_us", "speedup_attn_vs_dense", "speedup_step_vs_dense", "effective_hbm_gbs")
-        log("budget sweep: replay-shaped layer, 1 x 29504 tokens")
-        c1 = synth.replay_decode()
-        sweep = []
-        for scoring in ("envelope", "centroid"):
-            for k in (256, 512):
-                b1 = DecodeBench(c1, ops.Budget.topk(k), scoring, dev, a.replicas_gib)
-                rec = record(f"replay-shaped decode, 1 x 29504 tokens, {scoring}, top-{k} pages ({16 * k} tokens)",
-                             b1, b1.measure(100, 10))
-                sweep.append({k_: rec[k_] for k_ in keep})
-                del b1
-                torch.cuda.empty_cache()
-        del c1
-        res["budget_sweep"] = sweep
-        log("token-budget sweep: variable chunks, 1 x 29504 tokens")
-        c2 = synth.varchunk_decode()
-        tsa = []
-        for tokens in (4096, 8192, 16384):
-            b2 = ChunkedDecodeBench(c2, ops.Budget.token_budget(tokens), dev, a.replicas_gib)
-            tsa.append(b2.measure(100, 10))
-            del b2
-            torch.cuda.empty_cache()
-        del c2
-        res["chunk_budget_sweep"] = tsa
-        log("ratio sweep: 16 sequences of 8K-32K tokens, 64 q / 8 KV heads")
-        c3 = synth.batched_decode()
-        sweep = []
-        ratios = [float(x) for x in a.extra_ratios.split(",")] if a.extra_ratios else synth.RATIOS
-        for scoring, bos in (("centroid", 1), ("envelope", 0)):
-            for ratio in ratios:
-                b3 = DecodeBench(c3, ops.Budget.ratio_budget(ratio, bos, 1), scoring, dev, a.replicas_gib)
-                rec = record(f"batched decode, ratio {ratio}, {scoring}", b3, b3.measure(40, 5))
-                sweep.append({k: rec[k] for k in keep})
-                del b3
-                torch.cuda.empty_cache()
-        res["ratio_sweep"] = sweep
     if a.calibration_copy_mib:
         n = a.calibration_copy_mib * 2 ** 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -772,7 +956,8 @@ def main():
         log(f"calibration copy of {n} bytes done")
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(case, k_pages, a.scoring, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(head_case, a.budget // 16, a.scoring, a.cpu_seconds, a.cpu_seconds_1t,
+                                           attended)
     print(json.dumps(res), flush=True)
 
 

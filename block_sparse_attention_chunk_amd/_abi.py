@@ -54,6 +54,8 @@ SIGNATURES = {
     "bsa_sparse_attn_decode": (ctypes.c_int, [_P, _i32, _KV, _CH, _P, _P, _i32, _f32, _i32, _P, _P, _sz, _P]),
     "bsa_decode_merge": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32, _P, _P]),
     "bsa_select_attn_decode": (ctypes.c_int, [_P, _i32, _KV, _P, _BG, _f32, _i32, _P, _P, _P, _i32, _P, _sz, _P]),
+    "bsa_decode_step_workspace_bytes": (_sz, [_KV, _i32, _BG, _i32]),
+    "bsa_decode_step": (ctypes.c_int, [_P, _i32, _KV, _MT, _i32, _BG, _f32, _i32, _P, _P, _P, _P, _i32, _P, _sz, _P]),
     "bsa_select_attn_decode_static": (ctypes.c_int, [_P, _i32, _KV, _P, _BG, _f32, _i32, _P, _P, _P, _i32, _P]),
     "bsa_tile_prefill_workspace_bytes": (ctypes.c_size_t, [_KV, _i32]),
     "bsa_sparse_attn_tile_prefill": (ctypes.c_int, [_P, _i32, _i32, _KV, _i32, _P, _i32, _f32, _P, _P, ctypes.c_size_t,

@@ -398,13 +398,13 @@ struct FusedPlan {
     size_t ws_need;     // workspace bytes the launch uses
 };
 
-static int plan_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const float *scores,
-                                   const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out,
-                                   int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, FusedPlan *p) {
+static int plan_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_budget *budget,
+                                   float softmax_scale, int32_t num_splits, float *out, int32_t *sel_idx,
+                                   int32_t *sel_count, int32_t max_sel, FusedPlan *p) {
     int rc = check_kv(kv, true, &p->v);
     if (rc) return rc;
     if ((rc = check_heads(kv, num_q_heads, 16))) return rc;
-    if (!q || !scores || !budget) return fail(BSA_ERR_INVALID_ARG, "q, scores and budget must be non-NULL");
+    if (!q || !budget) return fail(BSA_ERR_INVALID_ARG, "q and budget must be non-NULL");
     if (!aligned16(q)) return fail(BSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
     if (kv->page_size != 16) return fail(BSA_ERR_UNSUPPORTED, "fused selection needs 16-token pages");
     if (kv->max_pages > kMaxSelectChunks)
@@ -472,13 +472,77 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
                            int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace,
                            size_t workspace_bytes, void *stream) {
     FusedPlan p;
-    int rc = plan_select_attn_decode(q, num_q_heads, kv, scores, budget, softmax_scale, num_splits, out, sel_idx,
-                                     sel_count, max_sel, &p);
+    if (!scores) return fail(BSA_ERR_INVALID_ARG, "scores must be non-NULL");
+    int rc = plan_select_attn_decode(q, num_q_heads, kv, budget, softmax_scale, num_splits, out, sel_idx, sel_count,
+                                     max_sel, &p);
     if (rc) return rc;
     if (p.ws_need && (!workspace || workspace_bytes < p.ws_need))
         return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", p.ws_need, workspace_bytes);
     if (p.ws_need && !aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     return launch_select_attn_decode(p, q, num_q_heads, kv, scores, budget, softmax_scale, out, sel_idx, sel_count,
+                                     max_sel, workspace, stream);
+}
+
+// ---- one decode step: scoring, then selection + attention + merge ------------
+static size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+struct StepPlan {
+    FusedPlan f;
+    bsa::ChunkView c;
+    size_t scores_off, total;
+};
+
+static int plan_decode_step(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_meta *meta,
+                            int32_t score_kind, const bsa_budget *budget, float softmax_scale, int32_t num_splits,
+                            float *out, int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, StepPlan *p) {
+    if (!out) return fail(BSA_ERR_INVALID_ARG, "out must be non-NULL");
+    int rc = plan_select_attn_decode(q, num_q_heads, kv, budget, softmax_scale, num_splits, out, sel_idx, sel_count,
+                                     max_sel, &p->f);
+    if (rc) return rc;
+    check_chunks(kv, nullptr, &p->c);
+    if (!meta) return fail(BSA_ERR_INVALID_ARG, "meta is NULL");
+    if (score_kind != BSA_ENVELOPE && score_kind != BSA_CENTROID)
+        return fail(BSA_ERR_INVALID_ARG, "score_kind %d is not BSA_ENVELOPE or BSA_CENTROID", score_kind);
+    if (score_kind == BSA_ENVELOPE && (!meta->kmin || !meta->kmax))
+        return fail(BSA_ERR_INVALID_ARG, "envelope scoring needs meta->kmin and meta->kmax");
+    if (score_kind == BSA_CENTROID && !meta->centroid)
+        return fail(BSA_ERR_INVALID_ARG, "centroid scoring needs meta->centroid");
+    if (!aligned16(meta->kmin) || !aligned16(meta->kmax) || !aligned16(meta->centroid))
+        return fail(BSA_ERR_INVALID_ARG, "meta arrays must be 16-byte aligned");
+    const size_t rows = (size_t)kv->batch * kv->num_kv_heads;
+    p->scores_off = al16(p->f.ws_need);
+    p->total = p->scores_off + al16(rows * kv->max_pages * sizeof(float));
+    return BSA_OK;
+}
+
+size_t bsa_decode_step_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, const bsa_budget *budget,
+                                       int32_t num_splits) {
+    if (!kv || !budget || kv->batch < 1 || kv->num_kv_heads < 1 || kv->max_pages < 1 || num_q_heads < 1) return 0;
+    int64_t need;
+    if (budget_need(budget, kv->max_pages, &need)) return 0;
+    const bool bal = balanced_applies(kv, (int)need, num_splits);
+    size_t ws = bal ? balanced_workspace_bytes(kv, num_q_heads) + balanced_list_bytes(kv, (int)need)
+                    : bsa_decode_workspace_bytes(kv, num_q_heads, (int)need, resolve_splits(kv, (int)need, num_splits));
+    const size_t rows = (size_t)kv->batch * kv->num_kv_heads;
+    return al16(ws) + al16(rows * kv->max_pages * sizeof(float));
+}
+
+int bsa_decode_step(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_meta *meta, int32_t score_kind,
+                    const bsa_budget *budget, float softmax_scale, int32_t num_splits, float *out, float *scores,
+                    int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    StepPlan p;
+    int rc = plan_decode_step(q, num_q_heads, kv, meta, score_kind, budget, softmax_scale, num_splits, out, sel_idx,
+                              sel_count, max_sel, &p);
+    if (rc) return rc;
+    if (!workspace || workspace_bytes < p.total)
+        return fail(BSA_ERR_WORKSPACE, "decode step workspace needs %zu bytes, got %zu", p.total, workspace_bytes);
+    if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    float *sc = scores ? scores : reinterpret_cast<float *>(static_cast<char *>(workspace) + p.scores_off);
+    hipError_t e = bsa::launch_score_decode(q, num_q_heads, p.f.v, p.c, meta->kmin, meta->kmax, meta->centroid,
+                                            score_kind, sc, (hipStream_t)stream);
+    if (e != hipSuccess) return launched(e);
+    return launch_select_attn_decode(p.f, q, num_q_heads, kv, sc, budget, softmax_scale, out, sel_idx, sel_count,
                                      max_sel, workspace, stream);
 }
 
@@ -518,8 +582,9 @@ int bsa_select_attn_decode_static(const void *q, int32_t num_q_heads, const bsa_
     if (!out) return fail(BSA_ERR_INVALID_ARG, "out must be non-NULL (partials in the static scratch are not "
                                                "reachable by the caller)");
     FusedPlan p;
-    int rc = plan_select_attn_decode(q, num_q_heads, kv, scores, budget, softmax_scale, num_splits, out, sel_idx,
-                                     sel_count, max_sel, &p);
+    if (!scores) return fail(BSA_ERR_INVALID_ARG, "scores must be non-NULL");
+    int rc = plan_select_attn_decode(q, num_q_heads, kv, budget, softmax_scale, num_splits, out, sel_idx, sel_count,
+                                     max_sel, &p);
     if (rc) return rc;
     if (p.ws_need > (size_t)BSA_STATIC_SCRATCH_BYTES)
         return fail(BSA_ERR_UNSUPPORTED,

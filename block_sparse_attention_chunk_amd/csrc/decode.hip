@@ -72,9 +72,12 @@ void decode_paged16_kernel(const T *__restrict__ q, int hq, KvView kv, const int
     uint4 qb[NW];
     load_q_operand<T, D>(q, hq, g, b, h, lane, qb);
     asm volatile("" : "+v"(spec_ld), "+v"(cnt_ld), "+v"(len_ld)::"memory");
-    if (items) spec = spec_ld;
     const int L = __builtin_amdgcn_readfirstlane(len_ld);
     const int npages = (L + 15) >> 4;
+    // kept page ids come from the caller: an id outside the row is clamped
+    // into it (wrong values, no stray address) rather than dereferenced
+    const int last_page = max(npages - 1, 0);
+    if (items) spec = min(max(spec_ld, 0), last_page);
     const int nitems = sel_idx ? min(max(__builtin_amdgcn_readfirstlane(cnt_ld), 0), max_sel) : npages;
     WaveState<T, D, GP> st;
     init_state(st);
@@ -88,7 +91,7 @@ void decode_paged16_kernel(const T *__restrict__ q, int hq, KvView kv, const int
     auto page_of = [&](int base) {
         if (base == 0) return spec;
         const int it = first + wstride * (base + (int)(threadIdx.x & 63));
-        return items ? items[min(it, max_sel - 1)] : it;
+        return items ? min(max(items[min(it, max_sel - 1)], 0), last_page) : it;
     };
     auto phys_of = [&](int, int page) { return bt ? bt[page] : b * kv.max_pages + page; };
     stream_pages<T, D, GP, PD>(st, qb, kv, kb, vb, L, n_mine, page_of, phys_of, scale_log2, region, lane);
@@ -135,7 +138,8 @@ __global__ __launch_bounds__(256) void decode_chunked_kernel(const T *__restrict
     };
     float *region = regions + w * R;
     for (int it = i0 + w; it < i1; it += kDecWaves) {
-        const int c = __builtin_amdgcn_readfirstlane(items ? items[it] : it);
+        // a caller's chunk id outside the row is clamped into it
+        const int c = __builtin_amdgcn_readfirstlane(items ? min(max(items[it], 0), max(nch - 1, 0)) : it);
         int s, e;
         if (ch.starts) {
             s = ch.starts[(int64_t)b * (ch.max_chunks + 1) + c];
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void decode_segments_kernel(const T *__rest
         const int i = threadIdx.x * PER + k;
         int s0 = 0, e0 = 0;
         if (i < nitems) {
-            const int c = items ? items[i] : i;
+            const int c = items ? min(max(items[i], 0), max(nch - 1, 0)) : i;   // caller ids clamped into the row
             if (cs) {
                 s0 = cs[c];
                 e0 = cs[c + 1];
@@ -432,6 +436,8 @@ void decode_balanced_kernel(const T *__restrict__ q, int hq, KvView kv, const in
         load_q_operand<T, D>(q, hq, g, b, h, lane, qb);
         asm volatile("" : "+v"(spec), "+v"(len_ld)::"memory");
         const int L = __builtin_amdgcn_readfirstlane(len_ld);
+        const int last_page = max(((L + 15) >> 4) - 1, 0);   // caller page ids are clamped into the row
+        spec = min(max(spec, 0), last_page);
         WaveState<T, D, GP> st;
         init_state(st);
         const T *kb = reinterpret_cast<const T *>(kv.k) + (int64_t)h * kv.sh;
@@ -439,7 +445,8 @@ void decode_balanced_kernel(const T *__restrict__ q, int hq, KvView kv, const in
         const int32_t *bt = kv.bt ? kv.bt + (int64_t)b * kv.max_pages : nullptr;
         auto page_of = [&](int base) {
             if (base == 0) return spec;
-            return items[min(first + kDecWaves * (base + (int)(threadIdx.x & 63)), max_sel - 1)];
+            return min(max(items[min(first + kDecWaves * (base + (int)(threadIdx.x & 63)), max_sel - 1)], 0),
+                       last_page);
         };
         auto phys_of = [&](int, int page) { return bt ? bt[page] : b * kv.max_pages + page; };
         stream_pages<T, D, GP, PD>(st, qb, kv, kb, vb, L, n_mine, page_of, phys_of, scale_log2, regions + w * R,
@@ -521,59 +528,15 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(const int32_t
     }
 }
 
-// Merge of the splits of one (sequence, query head):
-//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-// One wave per row; lane s holds split s's (m, l) (splits <= 64) and every
-// lane owns D/64 output dims.  All loads of a batch of 32 splits are issued
-// before the first use (clamped to the last split), so the kernel waits on
-// memory once per batch.
+// Merge of the splits of one (sequence, query head) per wave (the arithmetic
+// is merge_split_row in decode_common.h).
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(int splits, const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, float *__restrict__ out,
                                                           int hq) {
-    constexpr int VD = D / 64, SB = 32;
     args_ready(splits, part_o, part_ml, hq);
-    const int j = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const int64_t row = (int64_t)b * hq + j;
-    const float2 ml = reinterpret_cast<const float2 *>(part_ml + row * splits * 2)[min(lane, splits - 1)];
-    const float *po = part_o + row * splits * D + VD * lane;
-    float f = 0.f, lw = 0.f, acc[VD];
-#pragma unroll
-    for (int dd = 0; dd < VD; ++dd) acc[dd] = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += SB) {
-        float ov[SB][VD];
-#pragma unroll
-        for (int i = 0; i < SB; ++i) {
-            const float *p = po + (int64_t)min(s0 + i, splits - 1) * D;
-            if constexpr (VD == 2) {
-                const float2 x = *reinterpret_cast<const float2 *>(p);
-                ov[i][0] = x.x, ov[i][1] = x.y;
-            } else {
-                ov[i][0] = p[0];
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // every load of the batch is in flight before the first wait
-        if (s0 == 0) {
-            const float m = lane < splits ? ml.x : -INFINITY;
-            const float M = wave_max_all(m);
-            f = m == -INFINITY ? 0.f : exp2f(m - M);
-            lw = wave_sum_all(lane < splits ? f * ml.y : 0.f);
-        }
-        // split s's weight sits in lane s (0 for lanes >= splits)
-#pragma unroll
-        for (int i = 0; i < SB; ++i) {
-            const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(s0 + i, 63)));
-            const bool use = s0 + i < splits;
-#pragma unroll
-            for (int dd = 0; dd < VD; ++dd) acc[dd] = use ? fmaf(ws, ov[i][dd], acc[dd]) : acc[dd];
-        }
-    }
-    const float inv = 1.0f / lw;
-    if constexpr (VD == 2) {
-        reinterpret_cast<float2 *>(out + row * D)[lane] = make_float2(acc[0] * inv, acc[1] * inv);
-    } else {
-        out[row * D + lane] = acc[0] * inv;
-    }
+    const int j = blockIdx.x, b = blockIdx.y;
+    merge_split_row<D>(splits, part_o, part_ml, out, (int64_t)b * hq + j, threadIdx.x);
 }
 
 template <typename T, int D, int GP>

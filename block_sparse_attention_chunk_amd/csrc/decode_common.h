@@ -335,6 +335,59 @@ __device__ __forceinline__ void finish_workgroup(WaveState<T, D, GP> &st, float 
                                       part_ml);
 }
 
+// Merge of the splits of one (sequence, query head) row:
+//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+// One wave; lane s holds split s's (m, l) (splits <= 64) and every lane owns
+// D/64 output dims.  All loads of a batch of 32 splits are issued before the
+// first use (clamped to the last split), so the wave waits on memory once per
+// batch.
+template <int D>
+__device__ __forceinline__ void merge_split_row(int splits, const float *__restrict__ part_o,
+                                                const float *__restrict__ part_ml, float *__restrict__ out,
+                                                int64_t row, int lane) {
+    constexpr int VD = D / 64, SB = 32;
+    const float2 ml = reinterpret_cast<const float2 *>(part_ml + row * splits * 2)[min(lane, splits - 1)];
+    const float ml_m = ml.x, ml_l = ml.y;
+    const float *po = part_o + row * splits * D + VD * lane;
+    float f = 0.f, lw = 0.f, acc[VD];
+#pragma unroll
+    for (int dd = 0; dd < VD; ++dd) acc[dd] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += SB) {
+        float ov[SB][VD];
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+            const float *p = po + (int64_t)min(s0 + i, splits - 1) * D;
+            if constexpr (VD == 2) {
+                const float2 x = *reinterpret_cast<const float2 *>(p);
+                ov[i][0] = x.x, ov[i][1] = x.y;
+            } else {
+                ov[i][0] = p[0];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the batch is in flight before the first wait
+        if (s0 == 0) {
+            const float m = lane < splits ? ml_m : -INFINITY;
+            const float M = wave_max_all(m);
+            f = m == -INFINITY ? 0.f : exp2f(m - M);
+            lw = wave_sum_all(lane < splits ? f * ml_l : 0.f);
+        }
+        // split s's weight sits in lane s (0 for lanes >= splits)
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+            const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(s0 + i, 63)));
+            const bool use = s0 + i < splits;
+#pragma unroll
+            for (int dd = 0; dd < VD; ++dd) acc[dd] = use ? fmaf(ws, ov[i][dd], acc[dd]) : acc[dd];
+        }
+    }
+    const float inv = 1.0f / lw;
+    if constexpr (VD == 2) {
+        reinterpret_cast<float2 *>(out + row * D)[lane] = make_float2(acc[0] * inv, acc[1] * inv);
+    } else {
+        out[row * D + lane] = acc[0] * inv;
+    }
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void load_q_operand(const T *__restrict__ q, int hq, int g, int b, int h, int lane,
                                                uint4 (&qb)[DecTraits<T, D>::kNW]) {

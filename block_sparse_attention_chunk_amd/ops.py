@@ -19,7 +19,7 @@ from ._abi import (BSA_BF16, BSA_BUDGET_RATIO, BSA_BUDGET_TOKENS, BSA_BUDGET_TOP
 
 __all__ = ["upload", "KVCache", "Chunks", "Meta", "Budget", "build_chunk_meta", "score_chunks", "select_topk",
            "select_topk_router", "sparse_attn_decode", "sparse_attn_tile_prefill", "tile_prefill_workspace_bytes",
-           "decode_workspace_bytes",
+           "decode_workspace_bytes", "decode_step", "decode_step_workspace_bytes", "select_attn_decode",
            "router_workspace_bytes", "decode_num_splits"]
 
 
@@ -338,6 +338,37 @@ def select_attn_decode(q: torch.Tensor, kv: KVCache, scores: torch.Tensor, budge
                                   ctypes.byref(budget.struct()), float(scale), num_splits, _ptr(out), _ptr(sel_idx),
                                   _ptr(sel_count), max_sel, _ptr(workspace), ws_bytes, _stream(q.device))
     _abi.check(rc, "bsa_select_attn_decode")
+    return out
+
+
+def decode_step_workspace_bytes(kv: KVCache, num_q_heads: int, budget: Budget, num_splits: int = 0) -> int:
+    return int(_abi.lib().bsa_decode_step_workspace_bytes(ctypes.byref(kv.struct()), num_q_heads,
+                                                          ctypes.byref(budget.struct()), num_splits))
+
+
+def decode_step(q: torch.Tensor, kv: KVCache, meta: Meta, kind: int, budget: Budget, scale: Optional[float] = None,
+                num_splits: int = 0, out: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, sel_idx: Optional[torch.Tensor] = None,
+                sel_count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bsa_decode_step: chunk scores, selection, attention and split merge of
+    one decode step (16-token pages) in one call.  q [B][H_q][D] -> out
+    [B][H_q][D] float32; scores / sel_idx / sel_count, when given, receive
+    the chunk scores and the kept list."""
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = decode_step_workspace_bytes(kv, Hq, budget, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    max_sel = 0 if sel_idx is None else int(sel_idx.shape[2])
+    rc = _abi.lib().bsa_decode_step(_ptr(q), Hq, ctypes.byref(kv.struct()), ctypes.byref(meta.struct()), kind,
+                                    ctypes.byref(budget.struct()), float(scale), num_splits, _ptr(out), _ptr(scores),
+                                    _ptr(sel_idx), _ptr(sel_count), max_sel, _ptr(workspace), ws_bytes,
+                                    _stream(q.device))
+    _abi.check(rc, "bsa_decode_step")
     return out
 
 

@@ -309,6 +309,33 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
                            size_t workspace_bytes, void *stream);
 
 /*
+ * One whole decode step in one call ([P1] "The comparison": score every
+ * chunk against the query, keep the top chunks under the budget, attend only
+ * to them; [P2] ratio budget), for fixed 16-token pages: the chunk scores of
+ * bsa_score_chunks (score_kind BSA_ENVELOPE or BSA_CENTROID, meta as built
+ * by bsa_build_chunk_meta), then exactly what bsa_select_attn_decode does
+ * with out given (the fused selection + attention and the split merge, or
+ * on batches where the balanced schedule applies the selection kernel and
+ * the balanced attention).  out [batch][H_q][D] float32 is required and is
+ * bit-identical to bsa_score_chunks + bsa_select_attn_decode with the same
+ * num_splits (0 = automatic).  scores (nullable) receives the chunk scores
+ * [batch][H_kv][max_pages] as bsa_score_chunks writes them (else they stay
+ * in the workspace); sel_idx / sel_count (both or neither) receive the kept
+ * list as in bsa_select_attn_decode.  workspace (16-byte aligned, >=
+ * bsa_decode_step_workspace_bytes(kv, H_q, budget, num_splits) bytes) holds
+ * the split partials and the scores; it needs no initial contents, and
+ * calls sharing it must not overlap.  q, out 16-byte aligned; group size
+ * <= 16; max_pages <= 8192.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
+ */
+size_t bsa_decode_step_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, const bsa_budget *budget /* [host] */,
+                                       int32_t num_splits);
+int bsa_decode_step(const void *q, int32_t num_q_heads, const bsa_kv *kv, const bsa_meta *meta, int32_t score_kind,
+                    const bsa_budget *budget /* [host] */, float softmax_scale, int32_t num_splits, float *out,
+                    float *scores, int32_t *sel_idx, int32_t *sel_count, int32_t max_sel, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
  * bsa_select_attn_decode for callers that cannot allocate device memory or
  * pass a workspace (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same arguments, kernels and bits,

@@ -87,6 +87,21 @@ def _load():
     return _lib
 
 
+def _gomp():
+    _load()                      # the oracle library links the OpenMP runtime
+    return ctypes.CDLL("libgomp.so.1")
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads the oracle's parallel loops use from now on."""
+    _gomp().omp_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    """Threads the oracle's next parallel loop will use."""
+    return int(_gomp().omp_get_max_threads())
+
+
 def to_f64(x: np.ndarray) -> np.ndarray:
     """Widen an input to float64: uint16 arrays hold bfloat16 bit patterns
     (exact widening), float32 / float64 arrays are converted exactly."""

@@ -440,3 +440,82 @@ def test_empty_and_tiny_sequences(dev, fused):
     ref = oracle.decode_attn(case.q, oc, sel, cnt)
     assert np.all(np.isnan(out[0])) and np.all(np.isnan(ref[0]))
     assert max_abs(out[1:], ref[1:]) <= ATTN_ABS[case.dtype]
+
+
+def _clamp_case(case, sel, cnt, max_sel, rows):
+    """Corrupt a valid selection the way a careless caller could, so that the
+    clamped selection has no repeated page: rows = (full, no_first, no_last,
+    negative) name the rows that get a count past max_sel (their list is full),
+    a negative id (page 0 is not in their list), an id past the row (the last
+    page is not in their list) and a negative count.  Returns the corrupted
+    (sel, cnt) and the clamped equivalent the kernels must attend to."""
+    n = case.n_chunks()
+    bad_sel, bad_cnt = sel.copy(), cnt.copy()
+    full, no_first, no_last, neg = rows
+    gen = np.random.default_rng(len(sel.shape) + int(n.sum()))
+    for b, h in (no_first, no_last):   # lists without the row's first and last page
+        k = int(cnt[b, h])
+        bad_sel[b, h, :k] = np.sort(gen.choice(np.arange(1, n[b] - 1), size=k, replace=False))
+    sel = bad_sel.copy()
+    if full is not None:
+        b, h = full
+        assert cnt[b, h] == max_sel
+        bad_cnt[b, h] = max_sel + 9
+    b, h = no_first
+    assert cnt[b, h] >= 2 and 0 not in sel[b, h, :cnt[b, h]]
+    bad_sel[b, h, 0] = -7
+    b, h = no_last
+    assert cnt[b, h] >= 2 and n[b] - 1 not in sel[b, h, :cnt[b, h]]
+    bad_sel[b, h, cnt[b, h] - 1] = n[b] + 1000003
+    b, h = neg
+    bad_cnt[b, h] = -4
+    want_cnt = np.clip(bad_cnt, 0, max_sel).astype(np.int32)
+    want_sel = bad_sel.copy()
+    for b in range(case.batch):
+        for h in range(case.num_kv_heads):
+            k = want_cnt[b, h]
+            want_sel[b, h, :k] = np.clip(bad_sel[b, h, :k], 0, n[b] - 1)
+    return bad_sel, bad_cnt, want_sel, want_cnt
+
+
+@pytest.mark.parametrize("schedule", ["split-grid", "balanced", "segments", "per-token"])
+def test_out_of_range_selection_is_clamped(dev, schedule):
+    """Kept-page ids outside their row (negative, past the last page) and
+    counts outside [0, max_sel] in a caller's selection are clamped into range
+    by every decode schedule (the 16-token split grid, the balanced schedule,
+    the 16-token-segment kernel for 32-token pages, the per-token kernel for
+    8-token pages) rather than dereferenced: the output equals the oracle's on
+    the clamped selection, and a row whose count clamps to 0 is empty (NaN)."""
+    from block_sparse_attention_chunk_amd import ops
+    if schedule == "balanced":
+        case, sel, cnt = unequal_rows_case(23, synth.BF16, 128, 2102)
+        max_sel, splits = sel.shape[2], 0
+        rows = (None, (7, 1), (4, 1), (1, 0))
+    else:
+        page = {"split-grid": 16, "segments": 32, "per-token": 8}[schedule]
+        case = synth.make_decode(70 + page, batch=2, seq_lens=[300, 1001], num_q_heads=8, num_kv_heads=2,
+                                 head_dim=128, page_size=page, name=f"clamp-page{page}")
+        n = case.n_chunks()
+        max_sel = min(8, int(n.min()) - 1)
+        gen = np.random.default_rng(page)
+        sel = np.full((2, 2, max_sel), -1, np.int32)
+        cnt = np.full((2, 2), max_sel, np.int32)
+        for b in range(2):
+            for h in range(2):
+                pool = np.arange(1, n[b] - 1) if (b, h) != (0, 0) else np.arange(n[b])
+                sel[b, h] = np.sort(gen.choice(pool, size=max_sel, replace=False))
+        splits = 2
+        rows = ((0, 0), (0, 1), (1, 0), (1, 1))
+    log(f"clamped selection, schedule {schedule}")
+    bad_sel, bad_cnt, want_sel, want_cnt = _clamp_case(case, sel, cnt, max_sel, rows)
+    kv, _ = gpu_kv(case, dev)
+    q = ops.upload(case.q, dev)
+    out = _np(ops.sparse_attn_decode(q, kv, ops.upload(bad_sel, dev), ops.upload(bad_cnt, dev),
+                                     num_splits=splits))
+    torch.cuda.synchronize()
+    ref = oracle.decode_attn(case.q, oracle_cache(case), want_sel, want_cnt)
+    g = case.num_q_heads // case.num_kv_heads
+    empty = np.repeat(want_cnt == 0, g, axis=1)
+    assert np.all(np.isnan(out[empty])) and np.all(np.isnan(ref[empty]))
+    err = max_abs(out[~empty], ref[~empty])
+    assert err <= ATTN_ABS[case.dtype], err
