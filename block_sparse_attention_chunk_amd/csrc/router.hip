@@ -9,227 +9,309 @@
 //  step 4  sigma averaged over heads into one value per tile, triggered when it
 //          falls below a per-layer empirical quantile;
 //  step 5  triggered tiles attend to the top rho*k blocks, the others keep k and
-//          are padded with sentinels so every tile has the same dispatch shape.
+//          are padded with sentinels so every tile has the same dispatch shape;
+//          selection and expansion form one code path.
 // Readings: sigma per KV head (selection is per KV head); sigma = 0 when the top
 // k+1 scores tie; tiles seeing <= k blocks have no cut-off (sigma = 1, never
 // triggered, not part of the quantile); quantile by linear interpolation
 // between order statistics; strict '<'; sentinel -1 after ascending ids.
 //
-// Three launches: (1) one workgroup per (tile, KV head) selects the top
-// max(rho*k, k+1) blocks with the radix select of radix_select.h, sorts them (bitonic in LDS) and writes sigma plus the score-ordered
-// list; (2) one workgroup computes sigma_bar, the threshold and the trigger
-// flags (the path's only device-wide dependency); (3) one workgroup per
-// (tile, KV head) emits the ascending, sentinel-padded kv_idx row.
+// Two launches, no sorting:
+//  (1) router_select_kernel, one workgroup per (tile, KV head): the radix
+//      select of radix_select.h keeps the top max(rho*k, k+1) blocks of the
+//      score order, emitted in ascending block order; each kept block counts
+//      the kept blocks ranked above it (its rank in the score order), which
+//      gives s_(0), s_(k-1), s_(k) for sigma and splits the kept set into the
+//      top k (A) and ranks k .. rho*k-1 (B).  The kv_idx row is written as the
+//      expansion for both outcomes at once: A ascending, then B ascending,
+//      then -1.
+//  (2) router_finish_kernel, a few tiles per workgroup: every workgroup forms
+//      sigma_bar of all tiles and the quantile itself (a radix select of the
+//      order statistics over the eligible tiles; the same arithmetic in every
+//      workgroup, so every one finds the same threshold -- the only
+//      device-wide dependency of the router), then for its own tiles writes
+//      sigma_bar and the trigger flag and finishes the rows: an untriggered
+//      tile's row stops after A (sentinels over B), a triggered tile's row
+//      merges the two ascending runs in place.
 #include "bsa_internal.h"
 #include "radix_select.h"
 
 namespace bsa {
 
-constexpr int kRtThreads = 256;
 constexpr int kMaxList = 256;
 
 __device__ __forceinline__ int tile_visible(int t, int n_blocks, int causal) {
     return causal ? min(t + 1, n_blocks) : n_blocks;
 }
 
-// Bitonic sort of n2 (power of two, <= 256) 64-bit values in LDS, descending.
-__device__ void bitonic_desc_u64(uint64_t *v, int n2) {
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int i = threadIdx.x;
-            if (i < n2) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const bool desc = (i & size) == 0;
-                    const uint64_t a = v[i], c = v[j];
-                    if (desc ? (a < c) : (a > c)) {
-                        v[i] = c;
-                        v[j] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
 
-constexpr int kRtPer = 8;   // candidates per thread: up to 8 * NT blocks per tile
-
-template <int NT>
-__global__ __launch_bounds__(NT) void router_topk_kernel(const float *__restrict__ ts, int n_blocks, int hkv,
-                                                            int causal, int k, int rho, float *__restrict__ sigma,
-                                                            int32_t *__restrict__ top) {
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void router_select_kernel(const float *__restrict__ ts, int n_blocks, int hkv,
+                                                           int causal, int k, int rho, float *__restrict__ sigma,
+                                                           int32_t *__restrict__ kv_idx) {
     __shared__ RadixShared sh;
-    __shared__ uint32_t skeys[NT * kRtPer];
-    __shared__ int sel[kMaxList];
-    __shared__ uint64_t list[kMaxList];
+    __shared__ uint32_t kkey[kMaxList];   // kept blocks in ascending block order: key, id
+    __shared__ int kid[kMaxList];
+    __shared__ uint32_t rkey[3];          // keys at ranks 0, k-1, k
+    args_ready(ts, n_blocks, hkv, causal, k, rho, sigma, kv_idx);
     const int t = blockIdx.x, h = blockIdx.y;
     const int n = tile_visible(t, n_blocks, causal);
     const int width = rho * k;
     const int want = min(max(width, k + 1), n);
     const float *row = ts + ((int64_t)t * hkv + h) * n_blocks;
-    const int base = threadIdx.x * kRtPer;
-    uint32_t keys[kRtPer];
-    int wts[kRtPer];
+    const int base = threadIdx.x * PER;
+    float raw[PER];
 #pragma unroll
-    for (int i = 0; i < kRtPer; ++i) {
-        keys[i] = base + i < n ? float_key(row[base + i]) : 0u;
+    for (int i = 0; i < PER; ++i) raw[i] = row[min(base + i, n - 1)];   // visible blocks only
+    uint32_t keys[PER];
+    int wts[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        keys[i] = base + i < n ? float_key(raw[i]) : 0u;
         wts[i] = 1;
-        if (base + i < n) skeys[base + i] = keys[i];
     }
-    const int cnt = radix_select_prefix<NT, kRtPer>(keys, wts, base, n, want, true, sel, kMaxList, sh);
+    const int cnt = radix_select_prefix_emit<NT, PER>(
+        keys, wts, base, n, want, true, [](int) {},
+        [&](bool keep, int pos, int idx, int i) {
+            if (keep && pos < kMaxList) {
+                kkey[pos] = keys[i];
+                kid[pos] = idx;
+            }
+        },
+        sh);
     __syncthreads();
-    int n2 = 1;
-    while (n2 < cnt) n2 <<= 1;
-    for (int i = threadIdx.x; i < n2; i += NT)
-        list[i] = i < cnt ? ((uint64_t)skeys[sel[i]] << 32) | (uint64_t)(0xffffffffu - (uint32_t)sel[i]) : 0ull;
-    __syncthreads();
-    bitonic_desc_u64(list, n2);
-    int32_t *dst = top + ((int64_t)t * hkv + h) * width;
-    for (int i = threadIdx.x; i < width; i += NT)
-        dst[i] = i < min(cnt, width) ? (int32_t)(0xffffffffu - (uint32_t)(list[i] & 0xffffffffu)) : -1;
+    // rank of kept block p in the score order (descending key, lower block
+    // first): kept blocks sit in ascending block order, so an equal key ranks
+    // above p exactly when it sits before p
+    const int p = threadIdx.x;
+    int r = 0;
+    uint32_t kp = 0;
+    if (p < cnt) {
+        kp = kkey[p];
+        for (int q0 = 0; q0 < cnt; q0 += 16) {   // 16 reads in flight, then 16 compares
+            uint32_t kq[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) kq[j] = kkey[min(q0 + j, kMaxList - 1)];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int q = q0 + j;
+                r += (q < cnt && (kq[j] > kp || (kq[j] == kp && q < p))) ? 1 : 0;
+            }
+        }
+        if (r == 0) rkey[0] = kp;
+        if (r == k - 1) rkey[1] = kp;
+        if (r == k) rkey[2] = kp;
+    }
+    // positions: A = ranks < k, ascending; B = ranks k .. width-1, ascending
+    const bool in_a = p < cnt && r < k, in_b = p < cnt && r >= k && r < width;
+    int a = in_a ? 1 : 0, b = in_b ? 1 : 0, ta, tb;
+    block_scan_pair<NT>(a, b, sh, ta, tb);   // inclusive; totals |A|, |B|
+    int32_t *dst = kv_idx + ((int64_t)t * hkv + h) * width;
+    if (in_a) dst[a - 1] = kid[p];
+    if (in_b) dst[ta + b - 1] = kid[p];
+    for (int i = ta + tb + (int)threadIdx.x; i < width; i += NT) dst[i] = -1;
+    __syncthreads();   // rkey written
     if (threadIdx.x == 0) {
         double sg = 1.0;
         if (n > k) {
-            const double s0 = key_float((uint32_t)(list[0] >> 32));
-            const double sk1 = key_float((uint32_t)(list[k - 1] >> 32));
-            const double sk = key_float((uint32_t)(list[k] >> 32));
+            const double s0 = key_float(rkey[0]), sk1 = key_float(rkey[1]), sk = key_float(rkey[2]);
             sg = (s0 == sk) ? 0.0 : (sk1 - sk) / (s0 - sk);
         }
         sigma[(int64_t)t * hkv + h] = (float)sg;
     }
 }
 
-// One workgroup: sigma_bar, the quantile threshold over eligible tiles, trigger flags.
-constexpr int kQThreads = 1024;
-
-__global__ __launch_bounds__(kQThreads) void router_threshold_kernel(const float *__restrict__ sigma, int n_tiles,
-                                                                     int hkv, int n_blocks, int causal, int k,
-                                                                     float quantile, float fixed,
-                                                                     float *__restrict__ sigma_bar,
-                                                                     uint8_t *__restrict__ triggered,
-                                                                     float *__restrict__ threshold) {
-    extern __shared__ float vals[];   // next power of two >= n_tiles
-    __shared__ int cnt_s;
-    __shared__ double tau_s;
-    if (threadIdx.x == 0) cnt_s = 0;
-    __syncthreads();
-    auto mean_sigma = [&](int t) {
-        double acc = 0.0;
+// sigma_bar of tile t: the mean over KV heads in double (heads added in
+// order), stored as float.  HK > 0: the head count known at compile time, so
+// every load of a thread's candidates is in flight at once.
+template <int HK>
+__device__ __forceinline__ float sigma_mean(const float *__restrict__ sigma, int t, int hkv) {
+    double acc = 0.0;
+    if constexpr (HK > 0) {
+        float x[HK];
+#pragma unroll
+        for (int h = 0; h < HK; ++h) x[h] = sigma[(int64_t)t * HK + h];
+#pragma unroll
+        for (int h = 0; h < HK; ++h) acc += (double)x[h];
+        return (float)(acc / HK);
+    } else {
         for (int h = 0; h < hkv; ++h) acc += (double)sigma[(int64_t)t * hkv + h];
         return (float)(acc / hkv);
-    };
-    int n2 = 1;
-    while (n2 < n_tiles) n2 <<= 1;
-    // eligible values first (order irrelevant: they are sorted next), +inf padding
-    for (int t = threadIdx.x; t < n2; t += kQThreads) vals[t] = INFINITY;
-    __syncthreads();
-    for (int t = threadIdx.x; t < n_tiles; t += kQThreads) {
-        const float sb = mean_sigma(t);
-        sigma_bar[t] = sb;
-        if (tile_visible(t, n_blocks, causal) > k) {
-            const int slot = atomicAdd(&cnt_s, 1);
-            vals[slot] = sb;
-        }
-    }
-    __syncthreads();
-    const int m = cnt_s;
-    // ascending bitonic sort of n2 floats
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < n2; i += kQThreads) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const bool asc = (i & size) == 0;
-                    const float a = vals[i], c = vals[j];
-                    if (asc ? (a > c) : (a < c)) {
-                        vals[i] = c;
-                        vals[j] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-    if (threadIdx.x == 0) {
-        double tau;
-        if (!isnan(fixed)) {
-            tau = fixed;
-        } else if (m == 0) {
-            tau = NAN;
-        } else {
-            const double pos = (double)(m - 1) * (double)quantile;
-            const int lo = (int)floor(pos);
-            const double frac = pos - lo;
-            tau = lo + 1 < m ? (double)vals[lo] + frac * ((double)vals[lo + 1] - (double)vals[lo]) : (double)vals[lo];
-        }
-        tau_s = tau;
-        threshold[0] = (float)tau;
-    }
-    __syncthreads();
-    const double tau = tau_s;
-    for (int t = threadIdx.x; t < n_tiles; t += kQThreads) {
-        const bool elig = tile_visible(t, n_blocks, causal) > k;
-        triggered[t] = (elig && (double)mean_sigma(t) < tau) ? 1 : 0;
     }
 }
 
-__global__ __launch_bounds__(kRtThreads) void router_emit_kernel(const int32_t *__restrict__ top,
-                                                                 const uint8_t *__restrict__ triggered, int n_blocks,
-                                                                 int hkv, int causal, int k, int rho,
-                                                                 int32_t *__restrict__ kv_idx) {
-    __shared__ uint32_t v[kMaxList];
-    const int t = blockIdx.x, h = blockIdx.y;
+constexpr int kFinThreads = 512;
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kFinPer = 16;        // quantile candidates per thread: up to 8192 tiles
+constexpr int kFinRows = 32;       // (tile, KV head) rows finished per workgroup and round
+
+// Tiles per finishing workgroup: up to kFinRows rows (at least one tile).
+__host__ __device__ __forceinline__ int fin_tiles(int hkv) { return hkv >= kFinRows ? 1 : kFinRows / hkv; }
+
+template <int HK>
+__global__ __launch_bounds__(kFinThreads) void router_finish_kernel(const float *__restrict__ sigma, int n_tiles,
+                                                                    int hkv, int n_blocks, int causal, int k,
+                                                                    int rho, float quantile, float fixed,
+                                                                    float *__restrict__ sigma_bar,
+                                                                    uint8_t *__restrict__ triggered,
+                                                                    float *__restrict__ threshold,
+                                                                    int32_t *__restrict__ kv_idx) {
+    __shared__ RadixShared sh;
+    __shared__ float red[2][kFinWaves];
+    __shared__ int32_t rowbuf[kFinRows][kMaxList];
+    __shared__ float sb_s[kFinRows];
+    args_ready(sigma, n_tiles, hkv, n_blocks, causal, k, rho, quantile, fixed, kv_idx);
     const int width = rho * k;
-    const int n = tile_visible(t, n_blocks, causal);
-    const int keep = min(triggered[t] ? width : k, n);
-    int n2 = 1;
-    while (n2 < keep) n2 <<= 1;
-    const int32_t *src = top + ((int64_t)t * hkv + h) * width;
-    for (int i = threadIdx.x; i < n2; i += kRtThreads) v[i] = i < keep ? (uint32_t)src[i] : 0xffffffffu;
-    __syncthreads();
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int i = threadIdx.x;
-            if (i < n2) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const bool asc = (i & size) == 0;
-                    const uint32_t a = v[i], c = v[j];
-                    if (asc ? (a > c) : (a < c)) {
-                        v[i] = c;
-                        v[j] = a;
-                    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tpw = fin_tiles(hkv);
+    const int t0 = blockIdx.x * tpw;
+    const int nt_w = min(tpw, n_tiles - t0);
+    const int rows = nt_w * hkv;
+    // eligible tiles form the range [e0, n_tiles): causal tile t sees
+    // min(t + 1, n_blocks) blocks, so it has a cut-off exactly when t >= k
+    // (and n_blocks > k); every tile sees n_blocks blocks otherwise
+    const int e0 = n_blocks > k ? (causal ? min(k, n_tiles) : 0) : n_tiles;
+    const int m = n_tiles - e0;
+
+    // the first round of this workgroup's rows is requested before the
+    // threshold is known (it does not depend on it), and so is sigma_bar of
+    // its tiles
+    auto load_rows = [&](int r0) {
+        for (int rr = w; rr < min(kFinRows, rows - r0); rr += kFinWaves) {
+            const int t = t0 + (r0 + rr) / hkv, h = (r0 + rr) - ((r0 + rr) / hkv) * hkv;
+            const int32_t *row = kv_idx + ((int64_t)t * hkv + h) * width;
+            for (int i = lane; i < width; i += 64) rowbuf[rr][i] = row[i];
+        }
+    };
+    load_rows(0);
+    if ((int)threadIdx.x < nt_w) sb_s[threadIdx.x] = sigma_mean<HK>(sigma, t0 + threadIdx.x, hkv);
+
+    double tau;
+    if (!isnan(fixed)) {
+        tau = fixed;
+    } else if (m == 0) {
+        tau = NAN;
+    } else {
+        // order statistics lo and lo + 1 of the eligible sigma_bar (ascending):
+        // a radix select keeps the lo + 1 smallest (keys inverted), x_lo is the
+        // largest kept value and x_hi the smallest value not kept
+        const double pos = (double)(m - 1) * (double)quantile;
+        const int lo = (int)floor(pos);
+        const double frac = pos - lo;
+        const int base = threadIdx.x * kFinPer;
+        float v[kFinPer];
+        uint32_t keys[kFinPer];
+        int wts[kFinPer];
+#pragma unroll
+        for (int i = 0; i < kFinPer; ++i) {
+            const int c = base + i;
+            v[i] = c < m ? sigma_mean<HK>(sigma, e0 + c, hkv) : 0.f;
+            keys[i] = c < m ? ~float_key(v[i]) : 0u;
+            wts[i] = 1;
+        }
+        float kept_max = -INFINITY, rest_min = INFINITY;
+        radix_select_prefix_emit<kFinThreads, kFinPer>(
+            keys, wts, base, m, lo + 1, true, [](int) {},
+            [&](bool keep, int, int idx, int i) {
+                if (idx < m) {
+                    kept_max = keep ? fmaxf(kept_max, v[i]) : kept_max;
+                    rest_min = keep ? rest_min : fminf(rest_min, v[i]);
                 }
-            }
+            },
+            sh);
+        kept_max = wave_max_all(kept_max);
+        rest_min = -wave_max_all(-rest_min);
+        if (lane == 0) {
+            red[0][w] = kept_max;
+            red[1][w] = rest_min;
+        }
+        __syncthreads();
+        float x_lo = -INFINITY, x_hi = INFINITY;
+#pragma unroll
+        for (int i = 0; i < kFinWaves; ++i) {
+            x_lo = fmaxf(x_lo, red[0][i]);
+            x_hi = fminf(x_hi, red[1][i]);
+        }
+        tau = lo + 1 < m ? (double)x_lo + frac * ((double)x_hi - (double)x_lo) : (double)x_lo;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) threshold[0] = (float)tau;
+    __syncthreads();   // sb_s and the first round of rows are in LDS
+    if ((int)threadIdx.x < nt_w) {
+        const int t = t0 + threadIdx.x;
+        const float sb = sb_s[threadIdx.x];
+        sigma_bar[t] = sb;
+        triggered[t] = (t >= e0 && (double)sb < tau) ? 1 : 0;
+    }
+
+    // finish the rows, one wave per (tile, KV head) row
+    for (int r0 = 0; r0 < rows; r0 += kFinRows) {
+        if (r0 > 0) {
+            __syncthreads();   // every wave is done with the previous round
+            load_rows(r0);
             __syncthreads();
         }
+        for (int rr = w; rr < min(kFinRows, rows - r0); rr += kFinWaves) {
+            const int tl = (r0 + rr) / hkv, h = (r0 + rr) - tl * hkv, t = t0 + tl;
+            const int n = tile_visible(t, n_blocks, causal);
+            const int na = min(k, n), nb = min(width, n) - na;   // |A|, |B|
+            const bool trig = t >= e0 && (double)sb_s[tl] < tau;
+            int32_t *row = kv_idx + ((int64_t)t * hkv + h) * width;
+            if (!trig) {
+                for (int i = na + lane; i < na + nb; i += 64) row[i] = -1;
+                continue;
+            }
+            // merge A = row[0, na) and B = row[na, na + nb), both ascending and
+            // disjoint: an element's place is its index in its own run plus
+            // the number of smaller elements in the other run
+            const int32_t *buf = rowbuf[rr];
+            for (int i = lane; i < na + nb; i += 64) {
+                const int x = buf[i];
+                const bool from_a = i < na;
+                int lo2 = from_a ? na : 0, hi2 = from_a ? na + nb : na;   // search the other run
+                const int start = lo2;
+                while (lo2 < hi2) {
+                    const int mid = (lo2 + hi2) >> 1;
+                    if (buf[mid] < x) lo2 = mid + 1;
+                    else hi2 = mid;
+                }
+                row[(from_a ? i : i - na) + (lo2 - start)] = x;
+            }
+        }
     }
-    int32_t *dst = kv_idx + ((int64_t)t * hkv + h) * width;
-    for (int i = threadIdx.x; i < width; i += kRtThreads) dst[i] = i < keep ? (int32_t)v[i] : -1;
 }
 
 hipError_t launch_router(const float *ts, int32_t n_tiles, int32_t hkv, int32_t n_blocks, int32_t causal, int32_t k,
                          int32_t rho, float quantile, float fixed, int32_t *kv_idx, float *sigma, float *sigma_bar,
-                         uint8_t *triggered, float *threshold, void *ws, hipStream_t s) {
-    int32_t *top = (int32_t *)ws;
+                         uint8_t *triggered, float *threshold, void *, hipStream_t s) {
     dim3 grid(n_tiles, hkv);
-    if (n_blocks <= 256 * kRtPer)
-        hipLaunchKernelGGL(router_topk_kernel<256>, grid, dim3(256), 0, s, ts, n_blocks, hkv, causal, k, rho, sigma,
-                           top);
+    // the kept list (<= 256 blocks) needs one thread per kept block (measured
+    // at 131,072 tokens: 128 threads x 16 candidates 58 us for the router,
+    // one wave x 32 candidates 70 us)
+    const int want = max(rho * k, k + 1);
+    if (n_blocks <= 128 * 16 && want <= 128)
+        hipLaunchKernelGGL((router_select_kernel<128, 16>), grid, dim3(128), 0, s, ts, n_blocks, hkv, causal, k, rho,
+                           sigma, kv_idx);
+    else if (n_blocks <= 256 * 16)
+        hipLaunchKernelGGL((router_select_kernel<256, 16>), grid, dim3(256), 0, s, ts, n_blocks, hkv, causal, k, rho,
+                           sigma, kv_idx);
     else
-        hipLaunchKernelGGL(router_topk_kernel<1024>, grid, dim3(1024), 0, s, ts, n_blocks, hkv, causal, k, rho, sigma,
-                           top);
+        hipLaunchKernelGGL((router_select_kernel<1024, 8>), grid, dim3(1024), 0, s, ts, n_blocks, hkv, causal, k, rho,
+                           sigma, kv_idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int n2 = 1;
-    while (n2 < n_tiles) n2 <<= 1;
-    hipLaunchKernelGGL(router_threshold_kernel, dim3(1), dim3(kQThreads), (size_t)n2 * sizeof(float), s, sigma,
-                       n_tiles, hkv, n_blocks, causal, k, quantile, fixed, sigma_bar, triggered, threshold);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(router_emit_kernel, grid, dim3(kRtThreads), 0, s, top, triggered, n_blocks, hkv, causal, k, rho,
-                       kv_idx);
+    const int tpw = fin_tiles(hkv);
+    const dim3 fg((n_tiles + tpw - 1) / tpw), fb(kFinThreads);
+#define BSA_FIN(HK)                                                                                                \
+    hipLaunchKernelGGL(router_finish_kernel<HK>, fg, fb, 0, s, sigma, n_tiles, hkv, n_blocks, causal, k, rho, quantile, \
+                       fixed, sigma_bar, triggered, threshold, kv_idx)
+    switch (hkv) {
+    case 1: BSA_FIN(1); break;
+    case 2: BSA_FIN(2); break;
+    case 4: BSA_FIN(4); break;
+    case 8: BSA_FIN(8); break;
+    default: BSA_FIN(0); break;
+    }
+#undef BSA_FIN
     return hipGetLastError();
 }
 

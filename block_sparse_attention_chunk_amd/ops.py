@@ -249,13 +249,14 @@ def select_topk_router(tile_scores: torch.Tensor, k: int, rho: int, quantile: fl
     trig = torch.empty((nt,), dtype=torch.uint8, device=dev)
     thr = torch.empty((1,), dtype=torch.float32, device=dev)
     need = router_workspace_bytes(nt, H, k, rho)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L = _abi.lib()
     rc = L.bsa_select_topk_router(_ptr(tile_scores), nt, H, nb, int(bool(causal)), k, rho, float(quantile),
                                   float("nan") if fixed_threshold is None else float(fixed_threshold), _ptr(kv_idx),
-                                  _ptr(sigma), _ptr(sigma_bar), _ptr(trig), _ptr(thr), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(dev))
+                                  _ptr(sigma), _ptr(sigma_bar), _ptr(trig), _ptr(thr), _ptr(workspace), ws_bytes,
+                                  _stream(dev))
     _abi.check(rc, "bsa_select_topk_router")
     return {"kv_idx": kv_idx, "sigma": sigma, "sigma_bar": sigma_bar, "triggered": trig, "threshold": thr}
 

@@ -221,9 +221,14 @@ int bsa_select_topk(const float *scores, const bsa_kv *kv, const bsa_chunks *chu
  * ascending, padded with -1 to rho*k entries.
  * Outputs: kv_idx [num_tiles][H_kv][rho*k], sigma [num_tiles][H_kv],
  * sigma_bar [num_tiles], triggered [num_tiles] (0/1), threshold [1].
+ * Selection and expansion are one code path in two launches: per (tile, KV
+ * head) the top max(rho*k, k+1) blocks and sigma, written as the top k then
+ * the next rho*k - k blocks; then the threshold and triggers, and each row
+ * finished (cut after k, or the two runs merged into ascending order).
  * Limits: max(rho*k, k+1) <= 256, num_blocks <= 8192, num_tiles <= 8192.
- * workspace >= bsa_router_workspace_bytes(...).
- * Errors: INVALID_ARG, UNSUPPORTED (limits), WORKSPACE.
+ * The router needs no scratch: bsa_router_workspace_bytes() returns 0 and
+ * workspace may be NULL (kept in the signature for callers that pass one).
+ * Errors: INVALID_ARG, UNSUPPORTED (limits).
  */
 size_t bsa_router_workspace_bytes(int32_t num_tiles, int32_t num_kv_heads, int32_t k, int32_t rho);
 int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t num_kv_heads, int32_t num_blocks,

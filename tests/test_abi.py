@@ -208,15 +208,13 @@ def test_router_argument_checks():
         return L.bsa_select_topk_router(FAKE, nt, H, nb, 1, k, rho, quant, fixed, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
                                         wsb, None)
 
-    assert L.bsa_router_workspace_bytes(2048, 4, 32, 2) == 2048 * 4 * 64 * 4
+    assert L.bsa_router_workspace_bytes(2048, 4, 32, 2) == 0     # no scratch: lists go straight to kv_idx
     assert call(k=200, rho=2) == _abi.BSA_ERR_UNSUPPORTED
     assert call(k=256, rho=1) == _abi.BSA_ERR_UNSUPPORTED        # needs k+1 = 257 sorted scores
     assert call(nb=9000) == _abi.BSA_ERR_UNSUPPORTED
     assert call(nt=9000) == _abi.BSA_ERR_UNSUPPORTED
     assert call(quant=1.5) == _abi.BSA_ERR_INVALID_ARG
     assert call(k=0) == _abi.BSA_ERR_INVALID_ARG
-    assert call(ws=None) == _abi.BSA_ERR_WORKSPACE
-    assert call(wsb=8 * 2 * 4 * 4 - 1) == _abi.BSA_ERR_WORKSPACE
 
 
 def test_meta_and_score_argument_checks():

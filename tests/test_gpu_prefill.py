@@ -316,6 +316,47 @@ def test_router_prefill_full_size(dev, kind):
         f"fraction of (tile, head) with sigma < 0.05: {near:.3f}")
 
 
+@pytest.mark.parametrize("nt,H,nb,causal,k,rho,ties", [
+    (300, 3, 300, True, 100, 2, False),     # 200-entry rows, causal
+    (40, 2, 3000, False, 85, 3, False),     # 255-entry rows, 256-thread selection (> 2048 blocks)
+    (20, 1, 5000, False, 20, 2, False),     # 1024-thread selection (> 4096 blocks)
+    (64, 4, 64, True, 8, 2, True),          # integer scores: ties at every cut
+    (9, 1, 10, True, 4, 2, False),          # fewer tiles than a workgroup's share
+    (33, 2, 300, False, 255, 1, False),     # rho = 1 with k + 1 = 256 sorted scores
+])
+def test_router_on_synthetic_scores(dev, nt, H, nb, causal, k, rho, ties):
+    """The router alone on seeded tile scores, exactly against the oracle
+    router on the same scores: sigma, sigma_bar, threshold, trigger set and
+    the expanded, sentinel-padded kv_idx rows."""
+    from block_sparse_attention_chunk_amd import ops
+    g = np.random.default_rng(nt * 7 + k)
+    ts = (g.integers(0, 6, size=(nt, H, nb)) if ties else g.standard_normal((nt, H, nb))).astype(np.float32)
+    log(f"router on synthetic scores nt={nt} H={H} nb={nb} causal={causal} k={k} rho={rho} ties={ties}")
+    r = ops.select_topk_router(torch.tensor(ts, device=dev), k=k, rho=rho, causal=causal)
+    torch.cuda.synchronize()
+    nv = np.minimum(np.arange(nt) + 1, nb) if causal else np.full(nt, nb)
+    ref = oracle.router(ts.astype(np.float64), nv, k, rho)
+    sg, sb = _np(r["sigma"]), _np(r["sigma_bar"])
+    assert np.max(np.abs(sg - ref["sigma"])) <= 1e-6
+    assert np.max(np.abs(sb - ref["sigma_bar"])) <= 1e-6
+    elig = ref["eligible"]
+    tau = float(_np(r["threshold"])[0])
+    tau_ref = oracle.quantile(sb[elig].astype(np.float64), 0.25) if elig.any() else float("nan")
+    assert (np.isnan(tau) and np.isnan(tau_ref)) or abs(tau - tau_ref) <= 1e-6
+    trig = _np(r["triggered"]).astype(bool)
+    ref2 = oracle.router(ts.astype(np.float64), nv, k, rho, fixed_tau=tau_ref)   # oracle trigger at the GPU's values
+    clear = np.abs(sb.astype(np.float64) - tau_ref) > 1e-6
+    assert np.array_equal(trig[clear], ref2["triggered"][clear])
+    kv = _np(r["kv_idx"])
+    same = trig == ref["triggered"]
+    assert np.array_equal(kv[same], ref["kv_idx"][same])
+    for t in np.flatnonzero(~same):          # a trigger decided within 1e-6 of the threshold: still a valid row
+        for h in range(H):
+            keep = min(rho * k if trig[t] else k, nv[t])
+            row = kv[t, h]
+            assert np.all(np.diff(row[:keep]) > 0) and np.all(row[keep:] == -1)
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
 def test_tile_attention_group_sizes(dev, g):
     """Tile attention for every supported GQA group size on a ragged
