@@ -81,6 +81,7 @@ def parse():
     ap.add_argument("--only", choices=["headline", "h1b16", "h2", "ragged"], default=None,
                     help="profiling aid: run only this decode workload's timing loops and print its record")
     ap.add_argument("--kernel-launches", type=int, default=200, help="launches per per-kernel timing loop")
+    ap.add_argument("--samples", type=int, default=100, help="16-step replays timed for the step percentiles")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="profiling aid: after timing, copy this many MiB device-to-device once (a plain copy of "
                          "known size to scale HBM byte counters)")
@@ -310,7 +311,7 @@ class DecodeBench:
     def measure(self, steps, warmup, launches=200, samples=100):
         rot = self.rot
         t_step = rot.time_steps(self.step, steps, warmup)
-        pct = percentiles(rot.sample_steps(self.step, max(samples, steps)))
+        pct = percentiles(rot.sample_steps(self.step, samples))
         t_step_unfused = rot.time_steps(self.step_unfused, steps, warmup)
         self.step_unfused(0)
         self.torch.cuda.synchronize()
@@ -849,6 +850,21 @@ def budget_sweep(a, dev):
     return out
 
 
+def calibration_copy(a, dev):
+    """Profiling aid: one device-to-device copy of a known size, to scale the
+    HBM byte counters of the same run."""
+    if not a.calibration_copy_mib:
+        return
+    import torch
+    n = a.calibration_copy_mib * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy of {n} bytes done")
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -869,7 +885,7 @@ def main():
         case = make()
         b = DecodeBench(case, budget, scoring, dev, a.replicas_gib)
         steps = a.steps if key == "headline" else max(50, a.steps // 4)
-        m = b.measure(steps, a.warmup if key == "headline" else 5, a.kernel_launches)
+        m = b.measure(steps, a.warmup if key == "headline" else 5, a.kernel_launches, a.samples)
         recs[key] = (record(label, b, m), m)
         if key == "headline":
             head_case = case
@@ -877,6 +893,7 @@ def main():
         torch.cuda.empty_cache()
 
     if a.only:
+        calibration_copy(a, dev)
         print(json.dumps(recs[a.only][0]), flush=True)
         return
     head, m = recs["headline"]
@@ -946,14 +963,7 @@ def main():
             del lb, c
             torch.cuda.empty_cache()
         res["layer_stack"] = stacks
-    if a.calibration_copy_mib:
-        n = a.calibration_copy_mib * 2 ** 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {n} bytes done")
+    calibration_copy(a, dev)
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(head_case, a.budget // 16, a.scoring, a.cpu_seconds, a.cpu_seconds_1t,
