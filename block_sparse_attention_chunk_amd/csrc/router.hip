@@ -45,20 +45,12 @@ __device__ __forceinline__ int tile_visible(int t, int n_blocks, int causal) {
 }
 
 
+// Loads the n visible scores of one row (PER per thread, NT * PER >= n) and
+// keeps the top `want` of the score order in kkey / kid, in ascending block
+// order; returns the number kept.
 template <int NT, int PER>
-__global__ __launch_bounds__(NT) void router_select_kernel(const float *__restrict__ ts, int n_blocks, int hkv,
-                                                           int causal, int k, int rho, float *__restrict__ sigma,
-                                                           int32_t *__restrict__ kv_idx) {
-    __shared__ RadixShared sh;
-    __shared__ uint32_t kkey[kMaxList];   // kept blocks in ascending block order: key, id
-    __shared__ int kid[kMaxList];
-    __shared__ uint32_t rkey[3];          // keys at ranks 0, k-1, k
-    args_ready(ts, n_blocks, hkv, causal, k, rho, sigma, kv_idx);
-    const int t = blockIdx.x, h = blockIdx.y;
-    const int n = tile_visible(t, n_blocks, causal);
-    const int width = rho * k;
-    const int want = min(max(width, k + 1), n);
-    const float *row = ts + ((int64_t)t * hkv + h) * n_blocks;
+__device__ __forceinline__ int select_row(const float *__restrict__ row, int n, int want, RadixShared &sh,
+                                          uint32_t *kkey, int *kid) {
     const int base = threadIdx.x * PER;
     float raw[PER];
 #pragma unroll
@@ -70,7 +62,7 @@ __global__ __launch_bounds__(NT) void router_select_kernel(const float *__restri
         keys[i] = base + i < n ? float_key(raw[i]) : 0u;
         wts[i] = 1;
     }
-    const int cnt = radix_select_prefix_emit<NT, PER>(
+    return radix_select_prefix_emit<NT, PER>(
         keys, wts, base, n, want, true, [](int) {},
         [&](bool keep, int pos, int idx, int i) {
             if (keep && pos < kMaxList) {
@@ -79,6 +71,38 @@ __global__ __launch_bounds__(NT) void router_select_kernel(const float *__restri
             }
         },
         sh);
+}
+
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void router_select_kernel(const float *__restrict__ ts, int n_blocks, int hkv,
+                                                           int causal, int k, int rho, float *__restrict__ sigma,
+                                                           int32_t *__restrict__ kv_idx) {
+    __shared__ RadixShared sh;
+    __shared__ uint32_t kkey[kMaxList];   // kept blocks in ascending block order: key, id
+    __shared__ int kid[kMaxList];
+    __shared__ uint32_t rkey[3];          // keys at ranks 0, k-1, k
+    args_ready(ts, n_blocks, hkv, causal, k, rho, sigma, kv_idx);
+    // KV heads inner and the last tile first: a causal tile's work grows with
+    // its index, so the heaviest rows are dispatched first and the lightest
+    // fill the tail
+    const int h = blockIdx.x, t = gridDim.y - 1 - blockIdx.y;
+    const int n = tile_visible(t, n_blocks, causal);
+    const int width = rho * k;
+    const int want = min(max(width, k + 1), n);
+    const float *row = ts + ((int64_t)t * hkv + h) * n_blocks;
+    // a causal tile sees only the blocks up to its own, so earlier tiles take
+    // a quarter, a half or three quarters of the candidate slots per thread
+    // (the choice is uniform over the workgroup)
+    constexpr int P1 = PER >= 4 ? PER / 4 : 1, P2 = PER >= 2 ? PER / 2 : 1, P3 = PER >= 4 ? 3 * PER / 4 : PER;
+    int cnt;
+    if (n <= NT * P1)
+        cnt = select_row<NT, P1>(row, n, want, sh, kkey, kid);
+    else if (n <= NT * P2)
+        cnt = select_row<NT, P2>(row, n, want, sh, kkey, kid);
+    else if (n <= NT * P3)
+        cnt = select_row<NT, P3>(row, n, want, sh, kkey, kid);
+    else
+        cnt = select_row<NT, PER>(row, n, want, sh, kkey, kid);
     __syncthreads();
     // rank of kept block p in the score order (descending key, lower block
     // first): kept blocks sit in ascending block order, so an equal key ranks
@@ -148,6 +172,52 @@ constexpr int kFinRows = 32;       // (tile, KV head) rows finished per workgrou
 // Tiles per finishing workgroup: up to kFinRows rows (at least one tile).
 __host__ __device__ __forceinline__ int fin_tiles(int hkv) { return hkv >= kFinRows ? 1 : kFinRows / hkv; }
 
+// Order statistics lo and lo + 1 (ascending) of the eligible tiles'
+// sigma_bar, tiles [e0, e0 + m): a radix select keeps the lo + 1 smallest
+// (keys inverted); x_lo is the largest kept value and x_hi the smallest value
+// not kept.  FPER candidates per thread, kFinThreads * FPER >= m.
+template <int HK, int FPER>
+__device__ __forceinline__ void quantile_pair(const float *__restrict__ sigma, int e0, int m, int lo, int hkv,
+                                              RadixShared &sh, float (&red)[2][kFinWaves], float &x_lo,
+                                              float &x_hi) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int base = threadIdx.x * FPER;
+    float v[FPER];
+    uint32_t keys[FPER];
+    int wts[FPER];
+#pragma unroll
+    for (int i = 0; i < FPER; ++i) {
+        const int c = base + i;
+        v[i] = c < m ? sigma_mean<HK>(sigma, e0 + c, hkv) : 0.f;
+        keys[i] = c < m ? ~float_key(v[i]) : 0u;
+        wts[i] = 1;
+    }
+    float kept_max = -INFINITY, rest_min = INFINITY;
+    radix_select_prefix_emit<kFinThreads, FPER>(
+        keys, wts, base, m, lo + 1, true, [](int) {},
+        [&](bool keep, int, int idx, int i) {
+            if (idx < m) {
+                kept_max = keep ? fmaxf(kept_max, v[i]) : kept_max;
+                rest_min = keep ? rest_min : fminf(rest_min, v[i]);
+            }
+        },
+        sh);
+    kept_max = wave_max_all(kept_max);
+    rest_min = -wave_max_all(-rest_min);
+    if (lane == 0) {
+        red[0][w] = kept_max;
+        red[1][w] = rest_min;
+    }
+    __syncthreads();
+    x_lo = -INFINITY;
+    x_hi = INFINITY;
+#pragma unroll
+    for (int i = 0; i < kFinWaves; ++i) {
+        x_lo = fmaxf(x_lo, red[0][i]);
+        x_hi = fminf(x_hi, red[1][i]);
+    }
+}
+
 template <int HK>
 __global__ __launch_bounds__(kFinThreads) void router_finish_kernel(const float *__restrict__ sigma, int n_tiles,
                                                                     int hkv, int n_blocks, int causal, int k,
@@ -192,46 +262,16 @@ __global__ __launch_bounds__(kFinThreads) void router_finish_kernel(const float 
     } else if (m == 0) {
         tau = NAN;
     } else {
-        // order statistics lo and lo + 1 of the eligible sigma_bar (ascending):
-        // a radix select keeps the lo + 1 smallest (keys inverted), x_lo is the
-        // largest kept value and x_hi the smallest value not kept
         const double pos = (double)(m - 1) * (double)quantile;
         const int lo = (int)floor(pos);
         const double frac = pos - lo;
-        const int base = threadIdx.x * kFinPer;
-        float v[kFinPer];
-        uint32_t keys[kFinPer];
-        int wts[kFinPer];
-#pragma unroll
-        for (int i = 0; i < kFinPer; ++i) {
-            const int c = base + i;
-            v[i] = c < m ? sigma_mean<HK>(sigma, e0 + c, hkv) : 0.f;
-            keys[i] = c < m ? ~float_key(v[i]) : 0u;
-            wts[i] = 1;
-        }
-        float kept_max = -INFINITY, rest_min = INFINITY;
-        radix_select_prefix_emit<kFinThreads, kFinPer>(
-            keys, wts, base, m, lo + 1, true, [](int) {},
-            [&](bool keep, int, int idx, int i) {
-                if (idx < m) {
-                    kept_max = keep ? fmaxf(kept_max, v[i]) : kept_max;
-                    rest_min = keep ? rest_min : fminf(rest_min, v[i]);
-                }
-            },
-            sh);
-        kept_max = wave_max_all(kept_max);
-        rest_min = -wave_max_all(-rest_min);
-        if (lane == 0) {
-            red[0][w] = kept_max;
-            red[1][w] = rest_min;
-        }
-        __syncthreads();
-        float x_lo = -INFINITY, x_hi = INFINITY;
-#pragma unroll
-        for (int i = 0; i < kFinWaves; ++i) {
-            x_lo = fmaxf(x_lo, red[0][i]);
-            x_hi = fminf(x_hi, red[1][i]);
-        }
+        float x_lo, x_hi;
+        if (m <= kFinThreads * 4)
+            quantile_pair<HK, 4>(sigma, e0, m, lo, hkv, sh, red, x_lo, x_hi);
+        else if (m <= kFinThreads * 8)
+            quantile_pair<HK, 8>(sigma, e0, m, lo, hkv, sh, red, x_lo, x_hi);
+        else
+            quantile_pair<HK, kFinPer>(sigma, e0, m, lo, hkv, sh, red, x_lo, x_hi);
         tau = lo + 1 < m ? (double)x_lo + frac * ((double)x_hi - (double)x_lo) : (double)x_lo;
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) threshold[0] = (float)tau;
@@ -283,7 +323,7 @@ __global__ __launch_bounds__(kFinThreads) void router_finish_kernel(const float 
 hipError_t launch_router(const float *ts, int32_t n_tiles, int32_t hkv, int32_t n_blocks, int32_t causal, int32_t k,
                          int32_t rho, float quantile, float fixed, int32_t *kv_idx, float *sigma, float *sigma_bar,
                          uint8_t *triggered, float *threshold, void *, hipStream_t s) {
-    dim3 grid(n_tiles, hkv);
+    dim3 grid(hkv, n_tiles);
     // the kept list (<= 256 blocks) needs one thread per kept block (measured
     // at 131,072 tokens: 128 threads x 16 candidates 58 us for the router,
     // one wave x 32 candidates 70 us)

@@ -323,6 +323,12 @@ def test_router_prefill_full_size(dev, kind):
     (64, 4, 64, True, 8, 2, True),          # integer scores: ties at every cut
     (9, 1, 10, True, 4, 2, False),          # fewer tiles than a workgroup's share
     (33, 2, 300, False, 255, 1, False),     # rho = 1 with k + 1 = 256 sorted scores
+    # causal rows of every length, crossing each boundary of the candidate
+    # slots per thread (a quarter, half, three quarters or all of the
+    # workgroup's share) and of the quantile's slots (m <= 2048, 4096, more)
+    (1600, 2, 1600, True, 16, 2, False),    # 128-thread selection: 512 / 1024 / 1536 blocks
+    (2200, 1, 2200, True, 20, 2, False),    # 256-thread selection: 1024 / 2048 blocks
+    (5000, 1, 5000, True, 20, 2, False),    # 1024-thread selection: 2048 / 4096 blocks; m > 4096
 ])
 def test_router_on_synthetic_scores(dev, nt, H, nb, causal, k, rho, ties):
     """The router alone on seeded tile scores, exactly against the oracle
