@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the every-budget speedup records")
     ap.add_argument("--no-prefill", action="store_true", help="skip the router prefill records")
     ap.add_argument("--no-layers", action="store_true", help="skip the 48-layer decode-step records")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the gather-ceiling measurement beside the decode records")
     ap.add_argument("--sweep-ratios", type=str, default="",
                     help="comma-separated subset of the ragged batch's ratios (default: all seven)")
     ap.add_argument("--only", choices=["headline", "h1b16", "h2", "ragged"], default=None,
@@ -175,6 +177,77 @@ class Rotation:
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / (per * len(reps))
+
+
+class GatherCeiling:
+    """The bandwidth ceiling of the decode's read pattern: the bare gather
+    kernel of libbsa_ceiling.so reads distinct random 4 KiB runs (the size of
+    one K or V run of a (page, KV head)) from a 4 GiB buffer, as many bytes per
+    launch as a decode launch reads, with a fresh run list per launch (lists
+    rotate like cache replicas, >= 1 GiB per rotation).  Best of three wave
+    counts (256, 512, 1,024 workgroups of 4 waves), each timed like a kernel."""
+
+    BUF_BYTES = 4 << 30
+    RUN = 4096
+
+    def __init__(self, torch, dev, gib=1.0):
+        import ctypes
+        path = os.path.join(ROOT, "block_sparse_attention_chunk_amd", "libbsa_ceiling.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run python -m block_sparse_attention_chunk_amd.build")
+        self.lib = ctypes.CDLL(path)
+        f = self.lib.bsa_ceiling_gather
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                      ctypes.c_void_p]
+        f.restype = ctypes.c_int
+        self.torch, self.dev, self.gib = torch, dev, gib
+        self.buf = torch.empty(self.BUF_BYTES, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.cache = {}
+
+    def measure(self, nbytes):
+        torch = self.torch
+        n_runs = max(1, int(round(nbytes / self.RUN)))
+        if n_runs in self.cache:
+            return self.cache[n_runs]
+        R = replicas_for(n_runs * self.RUN, self.gib)
+        total = self.BUF_BYTES // self.RUN
+        g = torch.Generator(device=self.dev)
+        g.manual_seed(1000 + n_runs)
+        runs = torch.stack([torch.randperm(total, generator=g, device=self.dev)[:n_runs] for _ in range(R)])
+        runs = runs.to(torch.int32).contiguous()
+        assert int(runs.min()) >= 0 and int(runs.max()) < total   # every run inside the buffer
+        rot = Rotation(torch, self.dev, R)
+        best = None
+        for wgs in (256, 512, 1024):
+            per_wave = max(1, math.ceil(n_runs / (4 * wgs)))
+
+            def fn(r, per_wave=per_wave):
+                stream = torch.cuda.current_stream(self.dev).cuda_stream
+                rc = self.lib.bsa_ceiling_gather(self.buf.data_ptr(), runs[r].data_ptr(), n_runs, per_wave,
+                                                 self.sink.data_ptr(), stream)
+                if rc:
+                    raise RuntimeError(f"bsa_ceiling_gather failed: hip error {rc}")
+
+            t = rot.time_kernel(fn)
+            if best is None or t < best[0]:
+                best = (t, wgs)
+        res = {"bytes": n_runs * self.RUN, "us": best[0] * 1e6, "gbs": n_runs * self.RUN / best[0] / 1e9,
+               "workgroups": best[1], "run_lists": R}
+        self.cache[n_runs] = res
+        return res
+
+
+def attach_ceiling(rec, ceil, kv_bytes):
+    """The gather ceiling for the selected K/V bytes of one decode launch, and
+    the decode kernels' read rates as fractions of it."""
+    c = ceil.measure(kv_bytes)
+    rec["gather_ceiling"] = c
+    rec["selected_kv_of_ceiling"] = rec["selected_kv_gbs"] / c["gbs"]
+    if "fused_kernel_selected_kv_gbs" in rec:
+        rec["fused_kernel_of_ceiling"] = rec["fused_kernel_selected_kv_gbs"] / c["gbs"]
+    rec["attn_call_of_ceiling"] = rec["attn_selected_kv_gbs"] / c["gbs"]
+    return rec
 
 
 class DecodeBench:
@@ -582,6 +655,49 @@ class PrefillBench:
         }
 
 
+def torch_sdpa_causal(pc, dev, ours_dense_ms, repeats=3):
+    """An outside reference for the dense causal tile attention: torch's own
+    fused attention (scaled_dot_product_attention restricted to its flash
+    backend, causal, bf16 in and out, scale 1/sqrt(d)) on the same q / K / V,
+    K and V repeated over each KV head's query heads.  Timed with HIP events
+    (median of `repeats` after one warm-up call).  A backend that refuses the
+    shape leaves an explanation instead of a time."""
+    import torch
+    import torch.nn.functional as F
+    from block_sparse_attention_chunk_amd import ops
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+    except ImportError as e:
+        return {"available": False, "why": f"torch.nn.attention: {e}"}
+    g = pc.num_q_heads // pc.num_kv_heads
+    q = ops.upload(pc.q, dev).transpose(0, 1).unsqueeze(0).contiguous()                     # [1][Hq][T][D]
+    k = ops.upload(pc.k, dev).transpose(0, 1).repeat_interleave(g, dim=0).unsqueeze(0).contiguous()
+    v = ops.upload(pc.v, dev).transpose(0, 1).repeat_interleave(g, dim=0).unsqueeze(0).contiguous()
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            F.scaled_dot_product_attention(q, k, v, is_causal=True)
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(repeats):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                F.scaled_dot_product_attention(q, k, v, is_causal=True)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+    except RuntimeError as e:
+        return {"available": False, "why": str(e).splitlines()[0][:200]}
+    finally:
+        del q, k, v
+        torch.cuda.empty_cache()
+    t_ms = sorted(times)[len(times) // 2]
+    T, D = pc.T, pc.head_dim
+    flops = 4.0 * D * pc.num_q_heads * (T * (T + 1) / 2)          # exact causal count, QK^T + PV
+    return {"available": True, "what": "torch scaled_dot_product_attention, flash backend, causal, bf16",
+            "ms": t_ms, "tflops_exact_causal": flops / (t_ms * 1e-3) / 1e12,
+            "dense_tile_kernel_speedup": t_ms / ours_dense_ms}
+
+
 class LayerStackBench:
     """A serving-shaped decode step: `layers` replay-shaped layers, each with
     its own K/V cache and metadata (device copies of one generated layer),
@@ -799,8 +915,10 @@ def decode_workloads(seq_len, budget_tokens, scoring):
            lambda: synth.batched_decode(), ops.Budget.ratio_budget(0.5, 1, 1), "centroid")
 
 
-def budget_sweep(a, dev):
-    """Speedup over this build's dense kernel at every budget the pages use."""
+def budget_sweep(a, dev, ceil=None):
+    """Speedup over this build's dense kernel at every budget the pages use
+    (with the gather ceiling of each 16-token-page record when `ceil` is
+    given)."""
     import torch
     from block_sparse_attention_chunk_amd import ops, synth
     out = []
@@ -813,8 +931,9 @@ def budget_sweep(a, dev):
             b = DecodeBench(c1, ops.Budget.topk(k), scoring, dev, a.replicas_gib)
             m = b.measure_light(60, 5, t_dense=t_dense)
             t_dense = m["t_dense"]
-            out.append(record_light(f"replay-shaped decode, 1 x 29504 tokens, {scoring}, top-{k} pages", b, m,
-                                    f"{16 * k} tokens"))
+            rec = record_light(f"replay-shaped decode, 1 x 29504 tokens, {scoring}, top-{k} pages", b, m,
+                               f"{16 * k} tokens")
+            out.append(attach_ceiling(rec, ceil, m["kv_bytes"]) if ceil else rec)
             del b
             torch.cuda.empty_cache()
     del c1
@@ -842,8 +961,9 @@ def budget_sweep(a, dev):
             b = DecodeBench(c3, ops.Budget.ratio_budget(ratio, bos, 1), scoring, dev, a.replicas_gib)
             m = b.measure_light(30, 3, t_dense=t_dense)
             t_dense = m["t_dense"]
-            out.append(record_light(f"batched decode, 16 x U[8K, 32K], {scoring} (bos={bos}, eos=1), ratio {ratio}",
-                                    b, m, f"ratio {ratio}"))
+            rec = record_light(f"batched decode, 16 x U[8K, 32K], {scoring} (bos={bos}, eos=1), ratio {ratio}",
+                               b, m, f"ratio {ratio}")
+            out.append(attach_ceiling(rec, ceil, m["kv_bytes"]) if ceil else rec)
             del b
             torch.cuda.empty_cache()
     del c3
@@ -892,6 +1012,12 @@ def main():
         del b
         torch.cuda.empty_cache()
 
+    ceil = None
+    if not a.no_ceiling:
+        log("gather ceiling of the decode reads")
+        ceil = GatherCeiling(torch, dev, a.replicas_gib)
+        for key, (rec, mm) in recs.items():
+            attach_ceiling(rec, ceil, mm["kv_bytes"])
     if a.only:
         calibration_copy(a, dev)
         print(json.dumps(recs[a.only][0]), flush=True)
@@ -926,12 +1052,18 @@ def main():
                      "frac": head["fused_kernel_selected_kv_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": m["kv_bytes"],
                      "launch_us": m["t_fused_kernel"] * 1e6},
+        "practical_ceiling": ({"what": "bare gather of distinct random 4 KiB runs, the same bytes in one cold launch",
+                               "gbs": head["gather_ceiling"]["gbs"],
+                               "fused_kernel_frac": head["fused_kernel_of_ceiling"]}
+                              if "gather_ceiling" in head else None),
         "headline": head,
     }
     if not a.no_batched:
         res["batched"] = [recs[k][0] for k in ("h1b16", "h2", "ragged")]
     if not a.no_sweep:
-        res["budget_sweep"] = budget_sweep(a, dev)
+        res["budget_sweep"] = budget_sweep(a, dev, ceil)
+    del ceil
+    torch.cuda.empty_cache()
     attended = None
     if not a.no_prefill:
         log("router prefill: 131072 tokens")
@@ -939,6 +1071,8 @@ def main():
         pb = PrefillBench(pc, dev, ops.BSA_ENVELOPE)
         res["prefill"] = pb.measure()
         attended = res["prefill"]["attended_blocks"]
+        log("torch flash attention on the same prefill (outside reference)")
+        res["prefill"]["torch_sdpa_flash_causal"] = torch_sdpa_causal(pc, dev, res["prefill"]["dense_causal_attn_ms"])
         del pb, pc
         torch.cuda.empty_cache()
         by_len = []

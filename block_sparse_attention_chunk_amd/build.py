@@ -1,4 +1,5 @@
-"""Build libbsa.so (HIP, gfx950) in-tree with hipcc.
+"""Build libbsa.so (HIP, gfx950) in-tree with hipcc, and the benchmark's
+bandwidth-ceiling kernel libbsa_ceiling.so.
 
     python -m block_sparse_attention_chunk_amd.build [--jobs N]
 
@@ -19,6 +20,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
+# the benchmark's bandwidth-ceiling kernel, a library of its own
+CEILING_SRC = "ceiling.hip"
+CEILING_LIB = os.path.join(HERE, "libbsa_ceiling.so")
 
 SOURCES = ["api.cpp", "meta.hip", "score.hip", "select.hip", "router.hip", "decode.hip", "select_decode.hip", "tile_prefill.hip"]
 ARCH = "gfx950"
@@ -48,16 +52,21 @@ def _compile(src: str) -> str:
 def build(jobs: int = 8, verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(_compile, SOURCES + [CEILING_SRC]))
+    _link(objs[:-1], LIB, verbose)
+    _link(objs[-1:], CEILING_LIB, verbose)
+    return LIB
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libbsa.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
 
 
 def main(argv=None) -> int:
