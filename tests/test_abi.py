@@ -374,3 +374,24 @@ def test_static_scratch_entry_point_refuses_before_any_hip_call():
     assert call(big, 16, budget=top64) == _abi.BSA_ERR_UNSUPPORTED
     msg = L.bsa_last_error().decode()
     assert str(need) in msg and str(_abi.BSA_STATIC_SCRATCH_BYTES) in msg
+
+
+def test_ceiling_library_refuses_bad_arguments_before_any_hip_call():
+    """libbsa_ceiling.so (the benchmark's gather-ceiling kernel) exports its one
+    entry point and rejects missing buffers, empty run lists and a zero share
+    per wave on the host (hipErrorInvalidValue = 1), before any HIP call."""
+    path = os.path.join(os.path.dirname(_abi.LIB_PATH), "libbsa_ceiling.so")
+    if not os.path.exists(path):
+        pytest.skip("libbsa_ceiling.so not built")
+    lib = ctypes.CDLL(path)
+    f = lib.bsa_ceiling_gather
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    assert f(None, p, 4, 1, p, None) == 1
+    assert f(p, None, 4, 1, p, None) == 1
+    assert f(p, p, 4, 1, None, None) == 1
+    assert f(p, p, 0, 1, p, None) == 1
+    assert f(p, p, 4, 0, p, None) == 1
