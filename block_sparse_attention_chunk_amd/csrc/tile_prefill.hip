@@ -214,19 +214,35 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
         const char *vc = bcur + kPfBlockBytes;
         const bool diag = blk == t;
         // S^T for the 64 keys: 4 key tiles x 2 row tiles
+        // feature steps outermost, so the 8 accumulators of a step are
+        // independent MFMA chains; each step's 4 K operands are read one step
+        // ahead (measured 3 % faster than key tiles outermost with the reads
+        // next to their use; two steps ahead, or also reading V ahead, gained
+        // nothing).  Every accumulator still sums its steps in the same order.
         f32x4 s[4][2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const int key0 = 32 * (kt >> 1) + 4 * (kt & 1);  // + krow_lo (in koff)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) s[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto kread = [&](int kt, int st) {
+            const int key0 = 32 * (kt >> 1) + 4 * (kt & 1);  // + krow_lo (in koff)
+            return *reinterpret_cast<const bf16x8 *>(kc + key0 * kPfRowBytes + koff[st]);
+        };
+        bf16x8 ka[2][4];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kc + key0 * kPfRowBytes + koff[st]);
+        for (int kt = 0; kt < 4; ++kt) ka[0][kt] = kread(kt, 0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (st + 1 < 4) {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) ka[(st + 1) & 1][kt] = kread(kt, st + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep the next step's reads ahead of these MFMAs
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
-                    s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][st], s[kt][rt], 0, 0, 0);
-            }
+                    s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[st & 1][kt], qb[rt][st], s[kt][rt], 0, 0, 0);
         }
         // online softmax, one step per block and row.  Masks only where a key
         // can be invisible (the diagonal block, the ragged last block); the
