@@ -6,8 +6,10 @@ Workloads: the tiny fp32 decode; the 32:4-head, d 128 replay-shaped decode at
 29,504 tokens (budgets 4096 / 8192, envelope and centroid); the same with
 variable 16-256-token chunks (token budgets 4096 / 8192 / 16384 plus full
 context, and a 16,384-token instance whose 16,384 budget is dense); batched
-64:8-head decode with ragged lengths and the seven ratio budgets; NaN in the
-unused tail slots of partial pages; several split counts.
+64:8-head decode with ragged lengths and the seven ratio budgets; the
+benchmark's 32,768-token decode records at full size (one sequence, 16
+sequences, 64:8 heads at ratio 1/8); NaN in the unused tail slots of partial
+pages; several split counts.
 """
 import math
 
@@ -280,6 +282,28 @@ def test_batched_ratio_full_size(dev, kind, ratio):
         for h in range(case.num_kv_heads):
             s = r["sel"][b, h, :K]
             assert int(n[b]) - 1 in s and (not bos or 0 in s)
+
+
+@pytest.mark.parametrize("which", ["1x32k-top256", "16x32k-top256", "64q-8kv-16x32k-ratio-1/8"])
+def test_benchmark_decode_workloads_full_size(dev, which):
+    """The benchmark's decode records at their own sizes and in the launch
+    configuration it times (automatic splits; the fused call on its split
+    grid): one sequence of 32,768 tokens with the 4096-token budget, the same
+    layer over 16 sequences, and 64 q / 8 KV heads over 16 x 32,768 tokens at
+    ratio 1/8 with bos + eos.  Full parity against the oracle: metadata,
+    scores, selection (exact on the GPU's scores, band rule on the oracle's),
+    attention; dense attention too at one sequence."""
+    from block_sparse_attention_chunk_amd import ops
+    if which == "1x32k-top256":
+        case, kind, budget, forced = synth.replay_decode(seq_len=32768), ops.BSA_ENVELOPE, ops.Budget.topk(256), ()
+    elif which == "16x32k-top256":
+        case, kind, budget, forced = (synth.replay_decode(seq_len=32768, batch=16), ops.BSA_ENVELOPE,
+                                      ops.Budget.topk(256), ())
+    else:
+        case, kind, budget, forced = (synth.batched_decode(cid=3, seq_lens=[32768] * 16), ops.BSA_CENTROID,
+                                      ops.Budget.ratio_budget(0.125, 1, 1), ("bos", "eos"))
+    r = run_decode_case(case, dev, kind, budget, forced=forced, check_dense=which == "1x32k-top256")
+    assert np.all(r["cnt"] == budget.max_selected(2048))
 
 
 @pytest.mark.parametrize("dtype,D,hq", [("bf16", 128, 8), ("f32", 64, 8), ("bf16", 64, 32), ("f32", 128, 32)])
