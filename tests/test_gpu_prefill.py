@@ -329,6 +329,7 @@ def test_router_prefill_full_size(dev, kind):
     (1600, 2, 1600, True, 16, 2, False),    # 128-thread selection: 512 / 1024 / 1536 blocks
     (2200, 1, 2200, True, 20, 2, False),    # 256-thread selection: 1024 / 2048 blocks
     (5000, 1, 5000, True, 20, 2, False),    # 1024-thread selection: 2048 / 4096 blocks; m > 4096
+    (7000, 1, 7000, True, 20, 2, False),    # 1024-thread selection: 6144 blocks and past it
 ])
 def test_router_on_synthetic_scores(dev, nt, H, nb, causal, k, rho, ties):
     """The router alone on seeded tile scores, exactly against the oracle
