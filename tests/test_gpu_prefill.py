@@ -423,3 +423,36 @@ def test_tile_scores_group_sizes(dev, g, causal):
         assert np.array_equal(np.isfinite(ts), vis)
         err = np.abs(ts[vis] - ots[vis]) / oden[vis]
         assert err.max() <= SCORE_REL, err.max()
+
+
+def test_tile_attention_value_beyond_fp16_range_is_not_silent(dev):
+    """P.V runs in fp16, so a finite bf16 value beyond the fp16 range
+    (|v| > 65504) cannot be represented.  It is not dropped silently: every
+    row whose selected blocks contain it comes out non-finite (in the
+    value's KV head), and every other row stays finite and matches the
+    oracle."""
+    from block_sparse_attention_chunk_amd import ops
+    pc = synth.router_prefill(cid=131, T=640, num_q_heads=4, num_kv_heads=2, k=2, groups=4, tied_groups=(1,))
+    v = pc.v.copy()
+    tok, head = 200, 1                     # block 3, KV head 1
+    v[tok, head, 5] = 0x47c3               # bf16 bits of 99840.0: finite in bf16, beyond fp16
+    n_tiles = (pc.T + 63) // 64
+    kv_idx = np.full((n_tiles, 2, 2), -1, np.int32)
+    for t in range(n_tiles):
+        kv_idx[t, 0, :2 if t > 0 else 1] = [0, t] if t > 0 else [0]          # head 0: first and diagonal block
+        kv_idx[t, 1, :2 if t > 0 else 1] = [0, 1] if t > 0 else [0]          # head 1 avoids block 3 ...
+    kv_idx[6, 1, :2] = [3, 6]              # ... except tile 6, which attends to the block holding the value
+    log("tile attention with a value beyond the fp16 range")
+    kv = ops.KVCache(ops.upload(pc.k, dev), ops.upload(v, dev), torch.tensor([pc.T], dtype=torch.int32, device=dev),
+                     pc.block, token_major=True)
+    out = _np(ops.sparse_attn_tile_prefill(ops.upload(pc.q, dev), kv, torch.tensor(kv_idx, device=dev)))
+    torch.cuda.synchronize()
+    g = pc.num_q_heads // pc.num_kv_heads
+    bad_rows = np.arange(6 * 64, 7 * 64)
+    bad_heads = np.arange(head * g, (head + 1) * g)
+    assert not np.all(np.isfinite(out[np.ix_(bad_rows, bad_heads)]))
+    mask = np.ones(out.shape, bool)
+    mask[np.ix_(bad_rows, bad_heads)] = False
+    assert np.all(np.isfinite(out[mask]))
+    ref = oracle.tile_attn(pc.q, pc.k, v, num_kv_heads=2, block_size=64, tile_rows=64, kv_idx=kv_idx)
+    assert np.max(np.abs(out[mask] - ref[mask])) <= ATTN_ABS["bf16"]
