@@ -372,7 +372,10 @@ int bsa_select_attn_decode_static(const void *q, int32_t num_q_heads, const bsa_
  * baseline).  kv: batch 1, token-major bf16 [num_rows][H_kv][D] with
  * page_size == tile_rows == 64 and block_table NULL.  q [num_rows][H_q][D]
  * bf16; out [num_rows][H_q][D] float32.  Matrix-core kernel (bf16 Q.K^T,
- * fp16 P.V, fp32 accumulation; V must lie in the fp16 range).  Group size
+ * fp16 P.V, fp32 accumulation; V must lie in the fp16 range: a finite value
+ * beyond it, |v| > 65504, becomes infinite in the fp16 copy, and every row
+ * that attends to its block comes out non-finite in that KV head's query
+ * heads, never finite and wrong).  Group size
  * <= 8, head_dim 128, idx_stride <= 1024, stride_token < 2^24 elements.
  * workspace (16-byte aligned, >=
  * bsa_tile_prefill_workspace_bytes(kv, num_rows)) receives an fp16 copy of V
