@@ -123,7 +123,8 @@ int budget_need(const bsa_budget *budget, int max_chunks, int64_t *need) {
     }
 }
 
-constexpr int kMaxSelectChunks = 8192;
+constexpr int kMaxSelectChunks = 16384;   // candidates per row: 1024 threads x 16 in the selection kernel
+constexpr int kMaxFusedChunks = 8192;     // rows the fused kernel selects itself (512 threads x 16)
 constexpr int kMaxRouterBlocks = 8192;
 constexpr int kMaxRouterTiles = 8192;
 
@@ -165,6 +166,11 @@ size_t balanced_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads) {
     const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
     const size_t n = (size_t)(rows + bsa::kBalWgs) * (num_q_heads / kv->num_kv_heads) * (kv->head_dim + 2) * sizeof(float);
     return (n + 15) & ~(size_t)15;
+}
+
+// The split grid's partial outputs and (max, sum) pairs: none with one split.
+size_t partials_bytes(const bsa_kv *kv, int32_t num_q_heads, int splits) {
+    return splits <= 1 ? 0 : (size_t)kv->batch * num_q_heads * splits * (kv->head_dim + 2) * sizeof(float);
 }
 
 // The fused entry point on the balanced schedule keeps the kept lists (max
@@ -334,10 +340,13 @@ int32_t bsa_decode_num_splits(const bsa_kv *kv, int32_t num_q_heads, int32_t max
 size_t bsa_decode_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, int32_t max_items, int32_t num_splits) {
     const int s = bsa_decode_num_splits(kv, num_q_heads, max_items, num_splits);
     if (!kv || num_q_heads < 1 || kv->num_kv_heads < 1) return 0;
-    // partial outputs and (max, sum) pairs of every split
-    size_t n = s <= 1 ? 0 : (size_t)kv->batch * num_q_heads * s * (kv->head_dim + 2) * sizeof(float);
+    size_t n = partials_bytes(kv, num_q_heads, s);
     if (balanced_applies(kv, max_items, num_splits))
         n = std::max(n, balanced_workspace_bytes(kv, num_q_heads) + balanced_list_bytes(kv, max_items));
+    // the fused call on rows longer than its kernel selects keeps the kept
+    // lists after the partials
+    if (kv->page_size == 16 && kv->max_pages > kMaxFusedChunks)
+        n = std::max(n, ((n + 15) & ~(size_t)15) + balanced_list_bytes(kv, max_items));
     return n;
 }
 
@@ -385,6 +394,8 @@ int bsa_sparse_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
                                        workspace, (hipStream_t)stream));
 }
 
+static size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
+
 // The fused decode call's host side: every argument check and the launch
 // plan, without a HIP call, so the no-allocation variant can size its scratch
 // before touching the device.
@@ -392,6 +403,7 @@ struct FusedPlan {
     bsa::KvView v;
     int64_t need;       // the largest possible selection K
     bool balanced;      // selection kernel + balanced attention instead of the fused kernel
+    bool two_pass;      // selection kernel + split-grid attention (rows longer than the fused kernel selects)
     int splits;         // the fused kernel's split count
     size_t ws_need;     // workspace bytes the launch uses
 };
@@ -418,12 +430,24 @@ static int plan_select_attn_decode(const void *q, int32_t num_q_heads, const bsa
                     (long long)p->need);
     if (out && !aligned16(out)) return fail(BSA_ERR_INVALID_ARG, "out must be 16-byte aligned");
     p->balanced = out && balanced_applies(kv, (int)p->need, num_splits);
+    p->two_pass = false;
     if (p->balanced) {
         p->splits = 0;
         p->ws_need = balanced_workspace_bytes(kv, num_q_heads) + (sel_idx ? 0 : balanced_list_bytes(kv, (int)p->need));
         return BSA_OK;
     }
     p->splits = resolve_splits(kv, (int)p->need, num_splits);
+    if (kv->max_pages > kMaxFusedChunks) {
+        // rows longer than the fused kernel selects: the selection kernel,
+        // then the split-grid attention (the same kernels and bits as the two
+        // calls); the partials, then the kept lists when the caller takes none
+        if (!out && p->splits == 1)
+            return fail(BSA_ERR_INVALID_ARG, "out may be NULL only with more than one split (partials stay in the "
+                                             "workspace)");
+        p->two_pass = true;
+        p->ws_need = al16(partials_bytes(kv, num_q_heads, p->splits)) + (sel_idx ? 0 : balanced_list_bytes(kv, (int)p->need));
+        return BSA_OK;
+    }
     if ((p->need + p->splits - 1) / p->splits > kMaxItemsPerSplit)
         return fail(BSA_ERR_INVALID_ARG, "%d splits keep more than %d pages each; use more splits", p->splits,
                     kMaxItemsPerSplit);
@@ -460,6 +484,24 @@ static int launch_select_attn_decode(const FusedPlan &p, const void *q, int32_t 
                                             (hipStream_t)stream);
         return launched(e);
     }
+    if (p.two_pass) {
+        const size_t part = al16(partials_bytes(kv, num_q_heads, p.splits));
+        const int64_t rows = (int64_t)kv->batch * kv->num_kv_heads;
+        int32_t *si = sel_idx, *sc = sel_count;
+        int32_t ms = max_sel;
+        if (!si) {
+            si = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + part);
+            sc = si + rows * p.need;
+            ms = (int32_t)p.need;
+        }
+        bsa::ChunkView c;
+        check_chunks(kv, nullptr, &c);
+        hipError_t e = bsa::launch_select(scores, p.v, c, *budget, si, sc, ms, (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = bsa::launch_decode(q, num_q_heads, p.v, c, si, sc, ms, softmax_scale, p.splits, out,
+                                   part ? workspace : nullptr, (hipStream_t)stream);
+        return launched(e);
+    }
     return launched(bsa::launch_select_decode(q, num_q_heads, p.v, scores, *budget, sel_idx, sel_count,
                                               sel_idx ? max_sel : 0, softmax_scale, p.splits, out,
                                               p.ws_need ? workspace : nullptr, (hipStream_t)stream));
@@ -482,7 +524,6 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
 }
 
 // ---- one decode step: scoring, then selection + attention + merge ------------
-static size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
 
 struct StepPlan {
     FusedPlan f;

@@ -51,8 +51,11 @@ hipError_t launch_select(const float *scores, const KvView &kv, const ChunkView 
     if (ch.max_chunks <= 1024 * 2)
         hipLaunchKernelGGL((select_kernel<1024, 2>), grid, dim3(1024), 0, s, scores, kv, ch, b, sel_idx, sel_count,
                            max_sel);
-    else
+    else if (ch.max_chunks <= 1024 * 8)
         hipLaunchKernelGGL((select_kernel<1024, 8>), grid, dim3(1024), 0, s, scores, kv, ch, b, sel_idx, sel_count,
+                           max_sel);
+    else
+        hipLaunchKernelGGL((select_kernel<1024, 16>), grid, dim3(1024), 0, s, scores, kv, ch, b, sel_idx, sel_count,
                            max_sel);
     return hipGetLastError();
 }

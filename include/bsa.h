@@ -187,7 +187,7 @@ int bsa_score_chunks(const void *q, int32_t num_q_heads, int32_t num_rows, int32
  * Output: sel_idx [batch][H_kv][max_sel] chunk ids ascending, -1 after the
  * last; sel_count [batch][H_kv].  max_sel must hold the largest possible
  * count (TOPK: min(top_k, max_chunks); RATIO: the formula at max_chunks;
- * TOKENS: min(tokens, max_chunks)).  max_chunks <= 8192.
+ * TOKENS: min(tokens, max_chunks)).  max_chunks <= 16384.
  * Errors: INVALID_ARG (budget values, max_sel too small), UNSUPPORTED.
  */
 /*
@@ -297,13 +297,15 @@ int bsa_decode_merge(const void *workspace, int32_t batch, int32_t num_q_heads, 
  * selection K there).  With num_splits = 0 and out given on a batch where the
  * balanced schedule applies (see bsa_sparse_attn_decode, with K for max_sel),
  * this call runs the selection kernel of bsa_select_topk and then the
- * balanced attention instead of the fused kernel; the kept lists then stay in
- * the workspace unless sel_idx is given.  sel_idx / sel_count (both or neither) optionally receive the kept
+ * balanced attention instead of the fused kernel, and for max_pages > 8192 it
+ * runs that selection kernel and then bsa_sparse_attn_decode's split-grid
+ * attention (the fused kernel selects rows of at most 8192 pages); in both
+ * cases the kept lists stay in the workspace unless sel_idx is given.  sel_idx / sel_count (both or neither) optionally receive the kept
  * list as bsa_select_topk writes it (max_sel >= the largest possible
  * selection K).  Splits resolve as bsa_decode_num_splits(kv, H_q, K,
  * num_splits), num_splits in [0, 64], and each split keeps at most 2048
  * pages; workspace >= bsa_decode_workspace_bytes(kv, H_q, K, num_splits).
- * max_pages <= 8192; group size <= 16.  Calls sharing a workspace must not
+ * max_pages <= 16384; group size <= 16.  Calls sharing a workspace must not
  * overlap.  out may be NULL with more than one split, as for
  * bsa_sparse_attn_decode; q, out and workspace 16-byte aligned.
  * Errors: INVALID_ARG, UNSUPPORTED (page size, limits), WORKSPACE, LAUNCH.
@@ -330,7 +332,7 @@ int bsa_select_attn_decode(const void *q, int32_t num_q_heads, const bsa_kv *kv,
  * bsa_decode_step_workspace_bytes(kv, H_q, budget, num_splits) bytes) holds
  * the split partials and the scores; it needs no initial contents, and
  * calls sharing it must not overlap.  q, out 16-byte aligned; group size
- * <= 16; max_pages <= 8192.
+ * <= 16; max_pages <= 16384.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
  */
 size_t bsa_decode_step_workspace_bytes(const bsa_kv *kv, int32_t num_q_heads, const bsa_budget *budget /* [host] */,

@@ -196,7 +196,7 @@ def test_select_argument_checks():
     assert _select(kv, B(_abi.BSA_BUDGET_RATIO, 0, 0, 1, 1, 0.5), 31) == _abi.BSA_ERR_INVALID_ARG
     assert _select(kv, B(_abi.BSA_BUDGET_TOKENS, 0, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_INVALID_ARG
     assert _select(kv, B(9, 1, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_INVALID_ARG
-    assert _select(_kv(max_pages=9000), B(_abi.BSA_BUDGET_TOPK, 4, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_UNSUPPORTED
+    assert _select(_kv(max_pages=16385), B(_abi.BSA_BUDGET_TOPK, 4, 0, 0, 0, 0.0), 8) == _abi.BSA_ERR_UNSUPPORTED
     ch = _abi.bsa_chunks(FAKE, None, 10)
     assert _select(kv, B(_abi.BSA_BUDGET_TOPK, 4, 0, 0, 0, 0.0), 8, ctypes.byref(ch)) == _abi.BSA_ERR_INVALID_ARG
 
@@ -270,7 +270,18 @@ def test_fused_select_decode_argument_checks():
                                         FAKE if sel else None, FAKE if cnt else None, max_sel, ws, wsb, None)
 
     assert call(kv=_kv(page_size=32)) == _abi.BSA_ERR_UNSUPPORTED
-    assert call(kv=_kv(max_pages=9000)) == _abi.BSA_ERR_UNSUPPORTED
+    assert call(kv=_kv(max_pages=16385)) == _abi.BSA_ERR_UNSUPPORTED
+    # rows of more than 8192 pages: the selection kernel, then the split-grid
+    # attention; the kept lists (top-8: 8 + the count per row) follow the
+    # partials in the workspace unless sel_idx is given
+    long = _kv(max_pages=9000)
+    s9 = L.bsa_decode_num_splits(ctypes.byref(long), 8, 8, 0)
+    part = 1 * 8 * s9 * 130 * 4 if s9 > 1 else 0
+    lists = 1 * 2 * (8 + 1) * 4
+    need9 = L.bsa_decode_workspace_bytes(ctypes.byref(long), 8, 8, 0)
+    assert need9 == ((part + 15) & ~15) + lists
+    assert call(kv=long) == _abi.BSA_ERR_WORKSPACE
+    assert call(kv=long, ws=FAKE, wsb=need9 - 1) == _abi.BSA_ERR_WORKSPACE
     assert call(hq=34) == _abi.BSA_ERR_UNSUPPORTED
     assert call(sel=True) == _abi.BSA_ERR_INVALID_ARG                    # sel_idx without sel_count
     assert call(sel=True, cnt=True, max_sel=7) == _abi.BSA_ERR_INVALID_ARG  # 8 pages may be kept

@@ -306,6 +306,21 @@ def test_benchmark_decode_workloads_full_size(dev, which):
     assert np.all(r["cnt"] == budget.max_selected(2048))
 
 
+@pytest.mark.parametrize("budget_kind", ["top-256", "ratio-1/16"])
+def test_rows_longer_than_the_fused_selection(dev, budget_kind):
+    """262,144 cached tokens (16,384 pages) at one sequence: the selection
+    kernel takes rows of up to 16,384 candidates, and the fused entry point,
+    whose own kernel selects at most 8,192, runs that selection kernel and
+    then the split-grid attention -- bit-identical to the two calls.  Full
+    parity against the oracle, dense attention included."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.replay_decode(cid=17, seq_len=262144)
+    budget = ops.Budget.topk(256) if budget_kind == "top-256" else ops.Budget.ratio_budget(0.0625, 0, 1)
+    forced = () if budget_kind == "top-256" else ("eos",)
+    r = run_decode_case(case, dev, ops.BSA_ENVELOPE, budget, forced=forced, check_dense=budget_kind == "top-256")
+    assert np.all(r["cnt"] == budget.max_selected(16384))
+
+
 @pytest.mark.parametrize("dtype,D,hq", [("bf16", 128, 8), ("f32", 64, 8), ("bf16", 64, 32), ("f32", 128, 32)])
 def test_balanced_schedule_edges(dev, dtype, D, hq):
     """The balanced schedule (automatic splits, 16 rows with room for 4096

@@ -57,7 +57,7 @@ def _step_vs_two_calls(case, dev, kind, budget, splits=0, garbage=False, check_o
     return out
 
 
-@pytest.mark.parametrize("which", ["tiny-f32", "replay-6000-top64", "replay-32k-top256", "batched-4x"])
+@pytest.mark.parametrize("which", ["tiny-f32", "replay-6000-top64", "replay-32k-top256", "batched-4x", "replay-256k-top256"])
 def test_decode_step_matches_two_calls_and_oracle(dev, which):
     from block_sparse_attention_chunk_amd import ops
     if which == "tiny-f32":
@@ -66,6 +66,8 @@ def test_decode_step_matches_two_calls_and_oracle(dev, which):
         case, kind, budget = synth.replay_decode(cid=7, seq_len=6000), ops.BSA_CENTROID, ops.Budget.topk(64)
     elif which == "replay-32k-top256":
         case, kind, budget = synth.replay_decode(seq_len=32768), ops.BSA_ENVELOPE, ops.Budget.topk(256)
+    elif which == "replay-256k-top256":     # rows longer than the fused kernel selects: two passes
+        case, kind, budget = synth.replay_decode(cid=18, seq_len=262144), ops.BSA_CENTROID, ops.Budget.topk(256)
     else:
         case = synth.batched_decode(cid=15, batch=4, lo=3000, hi=9000)
         kind, budget = ops.BSA_ENVELOPE, ops.Budget.ratio_budget(0.125, 0, 1)

@@ -49,7 +49,7 @@ def _chunk_len(n, lens, n_max):
     return cl
 
 
-@pytest.mark.parametrize("n_max", [300, 2048, 5000])
+@pytest.mark.parametrize("n_max", [300, 2048, 5000, 12000])
 @pytest.mark.parametrize("mode", ["topk", "tokens", "ratio_bos_eos", "ratio_eos"])
 def test_selection_with_ties_is_exact(dev, n_max, mode):
     from block_sparse_attention_chunk_amd import ops
