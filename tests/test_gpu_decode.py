@@ -558,3 +558,48 @@ def test_out_of_range_selection_is_clamped(dev, schedule):
     assert np.all(np.isnan(out[empty])) and np.all(np.isnan(ref[empty]))
     err = max_abs(out[~empty], ref[~empty])
     assert err <= ATTN_ABS[case.dtype], err
+
+
+def _random_config(i):
+    """The i-th seeded configuration of the randomized sweep: shapes, dtype,
+    page size, ragged lengths, scoring, budget and split count drawn
+    together, so that combinations the fixed cases do not pair up are met."""
+    r = np.random.default_rng(9000 + i)
+    hkv = int(r.choice([1, 2, 3, 4]))
+    g = int(r.choice([1, 2, 3, 4, 5, 7, 8, 11, 16]))
+    D = int(r.choice([64, 128]))
+    dtype = str(r.choice(["bf16", "f32"]))
+    page = int(r.choice([16, 16, 16, 32, 64]))
+    batch = int(r.integers(1, 6))
+    lens = [int(x) for x in r.integers(1, 6000, size=batch)]
+    kind = str(r.choice(["envelope", "centroid"]))
+    budget = str(r.choice(["topk", "ratio", "tokens"]))
+    splits = int(r.choice([0, 0, 1, 2, 5, 13]))
+    return dict(hkv=hkv, g=g, D=D, dtype=dtype, page=page, batch=batch, lens=lens, kind=kind, budget=budget,
+                splits=splits)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_randomized_decode_configurations(dev, i):
+    """Seeded random decode configurations, each through the full oracle
+    comparison (metadata, scores, selection exact on the GPU's scores and by
+    the band rule on the oracle's, attention, dense attention, the fused call
+    bit for bit against the two calls on 16-token pages)."""
+    from block_sparse_attention_chunk_amd import ops
+    c = _random_config(i)
+    log(f"random config {i}: {c}")
+    case = synth.make_decode(9100 + i, batch=c["batch"], seq_lens=c["lens"], num_q_heads=c["hkv"] * c["g"],
+                             num_kv_heads=c["hkv"], head_dim=c["D"], page_size=c["page"], dtype=c["dtype"],
+                             channel_scale=(0.5, 4.0), name=f"random-{i}")
+    n_max = int(max((L + c["page"] - 1) // c["page"] for L in c["lens"]))
+    kd = ops.BSA_ENVELOPE if c["kind"] == "envelope" else ops.BSA_CENTROID
+    forced = ()
+    if c["budget"] == "topk":
+        budget = ops.Budget.topk(max(1, n_max // 5))
+    elif c["budget"] == "ratio":
+        budget = ops.Budget.ratio_budget(0.25, 1, 1)
+        forced = ("bos", "eos")
+    else:
+        budget = ops.Budget.token_budget(max(c["page"], n_max * c["page"] // 4))
+    splits = (0, c["splits"]) if c["splits"] else (0,)
+    run_decode_case(case, dev, kd, budget, forced=forced, splits=splits, band_exact_count=c["budget"] != "tokens")
