@@ -215,7 +215,8 @@ int bsa_select_topk(const float *scores, const bsa_kv *kv, const bsa_chunks *chu
  * with sigma = 0 when s_(0) == s_(k) and sigma = 1 (tile not eligible) when
  * n_t <= k.  sigma_bar[t] = mean over KV heads.  The threshold is the
  * `quantile` quantile (linear interpolation between order statistics) of
- * sigma_bar over eligible tiles, or fixed_threshold when it is not NaN;
+ * sigma_bar over eligible tiles (NaN when no tile is eligible), or
+ * fixed_threshold when it is not NaN;
  * triggered[t] = eligible && sigma_bar[t] < threshold.  kv_idx[t][h] holds
  * the first k blocks of the order (min(rho*k, n_t) when triggered),
  * ascending, padded with -1 to rho*k entries.

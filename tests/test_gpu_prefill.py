@@ -456,3 +456,63 @@ def test_tile_attention_value_beyond_fp16_range_is_not_silent(dev):
     assert np.all(np.isfinite(out[mask]))
     ref = oracle.tile_attn(pc.q, pc.k, v, num_kv_heads=2, block_size=64, tile_rows=64, kv_idx=kv_idx)
     assert np.max(np.abs(out[mask] - ref[mask])) <= ATTN_ABS["bf16"]
+
+
+def _random_prefill_config(i):
+    """The i-th seeded router-prefill configuration: length (ragged), KV
+    heads, group size, k, rho, quantile and scoring drawn together."""
+    r = np.random.default_rng(7000 + i)
+    return dict(T=int(r.integers(65, 5000)), hkv=int(r.choice([1, 2, 4])), g=int(r.integers(1, 9)),
+                k=int(r.integers(1, 13)), rho=int(r.choice([1, 2, 3])), quantile=float(r.choice([0.1, 0.25, 0.5, 0.9])),
+                kind=str(r.choice(["envelope", "centroid"])))
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_randomized_prefill_configurations(dev, i):
+    """Seeded random router prefills through the whole pipeline against the
+    oracle: block metadata, tile scores, the router on the GPU's scores
+    (exact away from the threshold) and against the oracle's own pipeline
+    (within the propagated score bound), and sparse and dense tile attention
+    on every row."""
+    from block_sparse_attention_chunk_amd import ops
+    c = _random_prefill_config(i)
+    k, rho, qp = c["k"], c["rho"], c["quantile"]
+    log(f"random prefill {i}: {c}")
+    pc = synth.router_prefill(cid=7100 + i, T=c["T"], num_q_heads=c["hkv"] * c["g"], num_kv_heads=c["hkv"], k=k,
+                              groups=4, tied_groups=(1, 3), rms_heads=(0,))
+    kd = ops.BSA_ENVELOPE if c["kind"] == "envelope" else ops.BSA_CENTROID
+    g, out, dout = gpu_prefill(pc, dev, kd, k, rho, quantile=qp, dense=True)
+    n_tiles = (pc.T + 63) // 64
+    omin, omax, ocen = block_meta_oracle(pc)
+    assert np.array_equal(oracle.to_f64(g["kmin"]), omin) and np.array_equal(oracle.to_f64(g["kmax"]), omax)
+    assert np.max(np.abs(g["cen"] - ocen)) <= 65 * 2.0 ** -24 * float(np.abs(oracle.to_f64(pc.k)).max())
+    okind = oracle.ENVELOPE if c["kind"] == "envelope" else oracle.CENTROID
+    ots, oden = oracle.tile_scores(pc.q, (omin, omax, ocen), okind, num_kv_heads=c["hkv"], tile_rows=64,
+                                   block_size=64)
+    vis = np.isfinite(ots)
+    assert np.array_equal(np.isfinite(g["ts"]), vis)
+    assert (np.abs(g["ts"][vis] - ots[vis]) / oden[vis]).max() <= SCORE_REL
+    # the router on the GPU's own scores
+    nv = np.minimum(np.arange(n_tiles) + 1, g["ts"].shape[2])
+    ref = oracle.router(g["ts"].astype(np.float64), nv, k, rho, quantile_p=qp)
+    assert np.max(np.abs(g["sigma"] - ref["sigma"])) <= 1e-6
+    assert np.max(np.abs(g["sigma_bar"] - ref["sigma_bar"])) <= 1e-6
+    elig = ref["eligible"]
+    if elig.any():
+        tau_ref = oracle.quantile(g["sigma_bar"][elig].astype(np.float64), qp)
+        assert abs(g["tau"] - tau_ref) <= 1e-6
+        ref2 = oracle.router(g["ts"].astype(np.float64), nv, k, rho, fixed_tau=tau_ref)
+        clear = np.abs(g["sigma_bar"].astype(np.float64) - tau_ref) > 1e-6
+        assert np.array_equal(g["triggered"][clear], ref2["triggered"][clear])
+        check_router_end_to_end(g, ots, oden, k, rho, qp)
+    else:                                    # no tile has a cut-off: nothing triggers
+        assert np.isnan(g["tau"]) and not g["triggered"].any()
+    same = g["triggered"] == ref["triggered"]
+    assert np.array_equal(g["kv_idx"][same], ref["kv_idx"][same])
+    # attention on the GPU's kv_idx, every row; dense causal
+    o = _np(out)
+    ref_o = oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=c["hkv"], block_size=64, tile_rows=64,
+                             kv_idx=g["kv_idx"])
+    assert max_abs(o, ref_o) <= ATTN_ABS["bf16"]
+    dref = oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=c["hkv"], block_size=64, tile_rows=64)
+    assert max_abs(_np(dout), dref) <= ATTN_ABS["bf16"]
