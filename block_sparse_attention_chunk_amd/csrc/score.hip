@@ -356,20 +356,23 @@ hipError_t launch_score_decode(const void *q, int32_t hq, const KvView &kv, cons
 }
 
 // ---------------------------------------------------------------------------
-// Query tiles on the matrix cores.  One workgroup per (tile t, KV head h),
-// one wave per query head of the group, 64 rows per wave (four 16-row MFMA
-// column tiles).  The block scores of a head form the product
+// Query tiles on the matrix cores.  One workgroup per (tile t, KV head h).
+// The group's G query heads x 64 rows form 4G row tiles of 16 rows, dealt
+// round-robin to NW = min(8, 4G) waves (wave w takes row tiles w, w + NW,
+// ...).  Waves w and w + 4 share a SIMD, so each SIMD carries G row tiles'
+// worth of matrix work (with one wave per head and G = 7 the busiest SIMD
+// would carry 8 of an average 7).  The block scores of a head form the product
 //     S^T[block][row] = sum_f A[block][f] * B[f][row]
 // over 2*D features: envelope A = [kmax | kmin], B = [q+ ; q-];
 // centroid A = [c_hi | c_lo] (float32 centroid split into two bf16 terms),
 // B = [q ; q].  bf16 inputs, fp32 accumulation (v_mfma_f32_16x16x32_bf16).
-// The wave's 64 rows are reduced by max in registers and across the 16 lanes
-// of a row group, the group's heads through LDS.  Metadata for 16 blocks is
-// staged in LDS and shared by all waves.
+// Every row of the group shares the K metadata (GQA), so a wave may mix heads.
+// A wave's rows are reduced by max in registers and across the 16 lanes of a
+// row group, the waves through LDS.  Metadata for 16 blocks is staged in LDS
+// and shared by all waves.
 // ---------------------------------------------------------------------------
 constexpr int kTileRows = 64;
 constexpr int kBlkTile = 16;               // blocks per MFMA row tile
-constexpr int kFeatRow = 2 * 128 + 8;      // staged bf16 features per block (+16 B pad)
 
 __device__ __forceinline__ uint4 split_sign(uint4 w, bool neg) {
     // keep the bf16 halves whose sign matches (neg: negative halves, else the rest)
@@ -396,54 +399,69 @@ constexpr int kStInstrs = kStTileBytes / 1024;
 
 __device__ __forceinline__ int st_slot(int row, int chunk) { return chunk ^ (row & 15); }
 
-// G waves (one per query head of the group).  Per tile: wait for this wave's
-// copies of it, one barrier, request the tile kStStages - 1 ahead into the
-// buffer everyone has just finished, then the tile's 32 MFMAs per wave, with
-// the previous tile's row maxima (vector ALU) interleaved so the matrix and
-// vector units work at the same time; the per-head maxima of the tile before
-// are combined after the next barrier.  No compiler-visible load sits in the
-// loop.  Tiles are taken in descending order, the causal ones with the most
-// blocks first.
-template <int KIND, int G>
-__global__ __launch_bounds__(64 * G) void score_tiles_kernel(const uint16_t *__restrict__ q, int hq, int rows,
-                                                             KvView kv, int n_blocks,
-                                                             const uint16_t *__restrict__ kmin,
-                                                             const uint16_t *__restrict__ kmax,
-                                                             const float *__restrict__ cen, int causal,
-                                                             float *__restrict__ out) {
-    constexpr int D = 128, PF = kStStages;
-    constexpr int NI = (kStInstrs + G - 1) / G;
-    __shared__ __attribute__((aligned(1024))) char ring[PF * kStTileBytes];
-    __shared__ float red[2][8][kBlkTile];
-    args_ready(q, hq, rows, kv.hkv, kv.page, n_blocks, kmin, kmax, cen, causal, out);
+template <int G>
+struct TileWaves {
+    static constexpr int NRT = 4 * G;                  // row tiles of the group
+    static constexpr int NW = NRT < 8 ? NRT : 8;       // waves
+    static constexpr int HI = (NRT + NW - 1) / NW;     // row tiles of waves w < NRT % NW (all, if 0)
+    static constexpr int LO = NRT / NW;
+    static constexpr int NI = (kStInstrs + NW - 1) / NW;  // staging instructions per wave and tile
+};
+
+struct TileScoreArgs {
+    const uint16_t *q;
+    int hq, rows;
+    KvView kv;
+    int n_blocks;
+    const uint16_t *kmin, *kmax;
+    const float *cen;
+    int causal;
+    float *out;
+};
+
+// One wave's part of a workgroup, for a wave that holds CNT row tiles.  Per
+// 16-block tile: wait for this wave's copies of it, one barrier, request the
+// tile kStStages - 1 ahead into the buffer everyone has just finished, then
+// the tile's 8 * CNT MFMAs, with the previous tile's row maxima (vector ALU)
+// interleaved so the matrix and vector units work at the same time; the
+// waves' maxima of the tile before are combined after the next barrier.  Every
+// wave passes the same barriers, whatever its CNT.  No compiler-visible load
+// sits in the loop.  Tiles are taken in descending order, the causal ones with
+// the most blocks first.
+template <int KIND, int G, int CNT>
+__device__ __forceinline__ void score_tiles_wave(const TileScoreArgs &A, char *ring, float (*red)[8][kBlkTile]) {
+    using TW = TileWaves<G>;
+    constexpr int D = 128, PF = kStStages, NW = TW::NW, NI = TW::NI;
     const int t = gridDim.x - 1 - blockIdx.x, h = blockIdx.y;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n16 = lane & 15, G4 = lane >> 4;
     const int r0 = t * kTileRows;
-    const int vis = causal ? min(n_blocks, (min(r0 + kTileRows, rows) - 1) / kv.page + 1) : n_blocks;
-    float *orow = out + ((int64_t)t * kv.hkv + h) * n_blocks;
-    const int64_t mbase = ((int64_t)h * n_blocks) * D;  // batch 1
+    const int vis = A.causal ? min(A.n_blocks, (min(r0 + kTileRows, A.rows) - 1) / A.kv.page + 1) : A.n_blocks;
+    float *orow = A.out + ((int64_t)t * A.kv.hkv + h) * A.n_blocks;
+    const int64_t mbase = ((int64_t)h * A.n_blocks) * D;  // batch 1
     const int ntiles16 = (vis + kBlkTile - 1) / kBlkTile;
 
-    // B operand: this wave's 64 rows (query head h*G + w), 8 k-steps of 32 features
-    bf16x8 bq[4][8];
-    bool rvalid[4];
+    // B operand: this wave's row tiles (row tile j: query head h*G + j/4,
+    // rows 16*(j%4) ..), 8 k-steps of 32 features
+    bf16x8 bq[CNT][8];
+    bool rvalid[CNT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int r = r0 + rt * 16 + n16;
-        rvalid[rt] = r < rows;
-        const uint32_t m = rvalid[rt] ? 0xffffffffu : 0u;
+    for (int i = 0; i < CNT; ++i) {
+        const int j = w + NW * i;
+        const int r = r0 + (j & 3) * 16 + n16;
+        rvalid[i] = r < A.rows;
+        const uint32_t m = rvalid[i] ? 0xffffffffu : 0u;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)min(r, rows - 1) * hq + h * G + w) * D + 32 * s +
-                                                       8 * G4);
+            uint4 v = *reinterpret_cast<const uint4 *>(A.q + ((int64_t)min(r, A.rows - 1) * A.hq + h * G + (j >> 2)) * D +
+                                                       32 * s + 8 * G4);
             v.x &= m, v.y &= m, v.z &= m, v.w &= m;
             if constexpr (KIND == BSA_ENVELOPE) {
-                bq[rt][s] = __builtin_bit_cast(bf16x8, split_sign(v, false));
-                bq[rt][s + 4] = __builtin_bit_cast(bf16x8, split_sign(v, true));
+                bq[i][s] = __builtin_bit_cast(bf16x8, split_sign(v, false));
+                bq[i][s + 4] = __builtin_bit_cast(bf16x8, split_sign(v, true));
             } else {
-                bq[rt][s] = __builtin_bit_cast(bf16x8, v);
-                bq[rt][s + 4] = bq[rt][s];
+                bq[i][s] = __builtin_bit_cast(bf16x8, v);
+                bq[i][s + 4] = bq[i][s];
             }
         }
     }
@@ -455,42 +473,43 @@ __global__ __launch_bounds__(64 * G) void score_tiles_kernel(const uint16_t *__r
         bt = min(bt, ntiles16 - 1);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int u = min(w + G * i, kStInstrs - 1);  // duplicates rewrite identical bytes
+            const int u = min(w + NW * i, kStInstrs - 1);  // duplicates rewrite identical bytes
             const int row = 2 * u + (lane >> 5);
             const int c = st_slot(row, lane & 31);
             const int blk = min(bt * kBlkTile + row, vis - 1);
             const char *src;
             if constexpr (KIND == BSA_ENVELOPE)
-                src = reinterpret_cast<const char *>((c < 16 ? kmax : kmin) + mbase + (int64_t)blk * D + 8 * (c & 15));
+                src = reinterpret_cast<const char *>((c < 16 ? A.kmax : A.kmin) + mbase + (int64_t)blk * D +
+                                                     8 * (c & 15));
             else
-                src = reinterpret_cast<const char *>(cen + mbase + (int64_t)blk * D + 4 * c);
+                src = reinterpret_cast<const char *>(A.cen + mbase + (int64_t)blk * D + 4 * c);
             dma16(src, lds_addr(ring) + stage * kStTileBytes + u * 1024);
         }
     };
-    // per-head maxima of tile bt -> the output row (wave 0, lanes 0..15)
+    // the waves' maxima of tile bt -> the output row (wave 0, lanes 0..15)
     auto finalize = [&](int bt) {
         if (threadIdx.x < kBlkTile) {
             const int blk = bt * kBlkTile + threadIdx.x;
             if (blk < vis) {
                 float m = red[bt & 1][0][threadIdx.x];
 #pragma unroll
-                for (int j = 1; j < G; ++j) m = fmaxf(m, red[bt & 1][j][threadIdx.x]);
+                for (int j = 1; j < NW; ++j) m = fmaxf(m, red[bt & 1][j][threadIdx.x]);
                 orow[blk] = m;
             }
         }
     };
 
-    auto mma = [&](int stage, f32x4 (&acc)[4]) {
+    auto mma = [&](int stage, f32x4 (&acc)[CNT]) {
         const char *fb = ring + stage * kStTileBytes + n16 * kStRowBytes;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < CNT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (KIND == BSA_ENVELOPE) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(fb + 16 * st_slot(n16, 4 * s + G4));
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[rt][s], acc[rt], 0, 0, 0);
+                for (int i = 0; i < CNT; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[i][s], acc[i], 0, 0, 0);
             }
         } else {
             // fp32 centroid dims 32s + 8G4 .. +8 -> bf16 hi (step s) and lo (step s + 4)
@@ -510,32 +529,32 @@ __global__ __launch_bounds__(64 * G) void score_tiles_kernel(const uint16_t *__r
                 const uint4 al = make_uint4(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16),
                                             lo[4] | (uint32_t(lo[5]) << 16), lo[6] | (uint32_t(lo[7]) << 16));
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), bq[rt][s],
-                                                                      acc[rt], 0, 0, 0);
-                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), bq[rt][s + 4],
-                                                                      acc[rt], 0, 0, 0);
+                for (int i = 0; i < CNT; ++i) {
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), bq[i][s], acc[i],
+                                                                     0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), bq[i][s + 4],
+                                                                     acc[i], 0, 0, 0);
                 }
             }
         }
     };
-    // lane holds S^T[block 4G4+i][row n16] of each row tile: maximum over the
-    // wave's 64 rows -> this head's slot of the tile's maxima
-    auto reduce = [&](const f32x4 (&acc)[4], int bt) {
+    // lane holds S^T[block 4G4+e][row n16] of each row tile: maximum over the
+    // wave's rows -> this wave's slot of the tile's maxima
+    auto reduce = [&](const f32x4 (&acc)[CNT], int bt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int e = 0; e < 4; ++e) {
             float m = -INFINITY;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) m = max_nn(m, rvalid[rt] ? acc[rt][i] : -INFINITY);
+            for (int i = 0; i < CNT; ++i) m = max_nn(m, rvalid[i] ? acc[i][e] : -INFINITY);
             m = row16_max(m);
-            red[bt & 1][w][4 * G4 + i] = m;  // every lane of the row holds the same maximum
+            red[bt & 1][w][4 * G4 + e] = m;  // every lane of the row holds the same maximum
         }
     };
     // the MFMAs of one tile and the row reduction of the previous one in a
     // single scheduling region, interleaved: one MFMA, then two vector ops
     auto interleave = [&]() {
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
+        for (int k = 0; k < 8 * CNT; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
@@ -551,7 +570,7 @@ __global__ __launch_bounds__(64 * G) void score_tiles_kernel(const uint16_t *__r
 
 #pragma unroll
     for (int p = 0; p < PF - 1; ++p) issue(p, p);
-    f32x4 accA[4], accB[4];
+    f32x4 accA[CNT], accB[CNT];
     int bt = 0;
     for (; bt + 1 < ntiles16; bt += 2) {
         top(bt);
@@ -580,7 +599,20 @@ __global__ __launch_bounds__(64 * G) void score_tiles_kernel(const uint16_t *__r
     stage_barrier();
     if (ntiles16 >= 2) finalize(ntiles16 - 2);
     finalize(ntiles16 - 1);
-    for (int blk = vis + threadIdx.x; blk < n_blocks; blk += 64 * G) orow[blk] = -INFINITY;
+    for (int blk = vis + threadIdx.x; blk < A.n_blocks; blk += 64 * NW) orow[blk] = -INFINITY;
+}
+
+template <int KIND, int G>
+__global__ __launch_bounds__(64 * TileWaves<G>::NW) void score_tiles_kernel(TileScoreArgs A) {
+    using TW = TileWaves<G>;
+    __shared__ __attribute__((aligned(1024))) char ring[kStStages * kStTileBytes];
+    __shared__ float red[2][8][kBlkTile];
+    args_ready(A.q, A.hq, A.rows, A.kv.hkv, A.kv.page, A.n_blocks, A.kmin, A.kmax, A.cen, A.causal, A.out);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (TW::HI == TW::LO || w < TW::NRT % TW::NW)
+        score_tiles_wave<KIND, G, TW::HI>(A, ring, red);
+    else
+        score_tiles_wave<KIND, G, TW::LO>(A, ring, red);
 }
 
 hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t tile_rows, const KvView &kv,
@@ -589,17 +621,15 @@ hipError_t launch_score_tiles(const void *q, int32_t hq, int32_t rows, int32_t t
     (void)tile_rows;  // validated to be 64 by the caller
     const int g = hq / kv.hkv;
     const int n_tiles = (rows + kTileRows - 1) / kTileRows;
-    dim3 grid(n_tiles, kv.hkv), block(64 * g);
+    const TileScoreArgs A{(const uint16_t *)q, hq, rows, kv, n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax,
+                          cen, causal, scores};
+    dim3 grid(n_tiles, kv.hkv);
 #define BSA_ST(G)                                                                                                   \
     case G:                                                                                                         \
         if (kind == BSA_ENVELOPE)                                                                                   \
-            hipLaunchKernelGGL((score_tiles_kernel<BSA_ENVELOPE, G>), grid, block, 0, s, (const uint16_t *)q, hq,   \
-                               rows, kv, n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal,     \
-                               scores);                                                                             \
+            hipLaunchKernelGGL((score_tiles_kernel<BSA_ENVELOPE, G>), grid, dim3(64 * TileWaves<G>::NW), 0, s, A);  \
         else                                                                                                        \
-            hipLaunchKernelGGL((score_tiles_kernel<BSA_CENTROID, G>), grid, block, 0, s, (const uint16_t *)q, hq,   \
-                               rows, kv, n_blocks, (const uint16_t *)kmin, (const uint16_t *)kmax, cen, causal,     \
-                               scores);                                                                             \
+            hipLaunchKernelGGL((score_tiles_kernel<BSA_CENTROID, G>), grid, dim3(64 * TileWaves<G>::NW), 0, s, A);  \
         break;
     switch (g) {
         BSA_ST(1) BSA_ST(2) BSA_ST(3) BSA_ST(4) BSA_ST(5) BSA_ST(6) BSA_ST(7) BSA_ST(8)
