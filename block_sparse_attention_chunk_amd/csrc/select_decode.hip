@@ -32,7 +32,7 @@ constexpr int kFusedListCap = 2048;  // kept pages per workgroup
 constexpr int kSmallGrid = 256;      // workgroups: one per compute unit
 
 template <typename T, int D, int GP, int PER, int NT>
-__global__ __launch_bounds__(NT, (sizeof(T) == 2 && NT == 256) ? 3 : 1)
+__global__ __launch_bounds__(NT, (sizeof(T) == 2 && NT == 256) ? (PER >= 32 ? 2 : 3) : 1)
 void select_decode_kernel(const T *__restrict__ q, int hq, KvView kv, const float *__restrict__ scores,
                           bsa_budget bud, int32_t *__restrict__ sel_idx, int32_t *__restrict__ sel_count,
                           int max_sel, float scale_log2, int splits, float *__restrict__ out,
@@ -134,7 +134,8 @@ static void launch_sd_t(const void *q, int hq, const KvView &kv, const float *sc
     // A grid of at most one workgroup per compute unit is latency-bound: 8
     // waves share the selection (half the candidates per thread), and the
     // first 4 attend as usual.  Larger grids keep 4 waves, so 3 workgroups fit
-    // on a compute unit.
+    // on a compute unit (2 with 32 candidates per thread, whose registers
+    // would otherwise spill).
     const int64_t wgs = (int64_t)splits * kv.hkv * kv.batch;
     if (wgs <= kSmallGrid) {
         if (kv.max_pages <= 512 * 4)

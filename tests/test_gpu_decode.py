@@ -448,6 +448,21 @@ def test_fused_long_rows(dev, seq_len, kind_budget):
     run_decode_case(case, dev, ops.BSA_ENVELOPE, budget, forced=forced, splits=(0, 7), check_dense=False)
 
 
+@pytest.mark.parametrize("seq_len,kind_budget", [(40000, "topk"), (70000, "ratio")])
+def test_fused_long_rows_large_grid(dev, seq_len, kind_budget):
+    """Rows of 2,500 and 4,375 pages on a grid of more than one workgroup
+    per compute unit (4 sequences x 4 KV heads x 17 splits): the fused
+    kernel's 4-wave form with 16 and 32 candidates per thread, against the
+    oracle and, bit for bit, against the two-call path."""
+    from block_sparse_attention_chunk_amd import ops
+    case = synth.make_decode(18, batch=4, seq_lens=[seq_len, seq_len - 999, seq_len // 2, seq_len - 16],
+                             num_q_heads=8, num_kv_heads=4, head_dim=128, channel_scale=(0.5, 4.0),
+                             name=f"long-grid-{seq_len}")
+    budget = ops.Budget.topk(300) if kind_budget == "topk" else ops.Budget.ratio_budget(1 / 16, 1, 1)
+    forced = () if kind_budget == "topk" else ("bos", "eos")
+    run_decode_case(case, dev, ops.BSA_ENVELOPE, budget, forced=forced, splits=(17,), check_dense=False)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_empty_and_tiny_sequences(dev, fused):
     """Degenerate rows: a sequence with no cached token (no chunk to keep: the
