@@ -254,7 +254,8 @@ int bsa_select_topk_router(const float *tile_scores, int32_t num_tiles, int32_t 
  * overlap.  sel_count entries are clamped to [0, max_sel] by every schedule
  * (the first max_sel entries are attended).  With more than one split, out
  * may be NULL: the merge is skipped and the workspace holds the partials
- * (layout at bsa_decode_merge).
+ * (layout at bsa_decode_merge).  A row with nothing to attend to (an empty
+ * sequence, a count of 0) comes out NaN: the softmax over an empty set.
  * Balanced schedule: with num_splits == 0, out != NULL, a selection, fixed
  * pages (chunks NULL or chunks->chunk_starts NULL), 16-token pages, 16 <= batch x H_kv <= 4096 and batch x H_kv x max_sel
  * >= 49152, the kept pages of all rows are laid end to end and cut into 256
@@ -372,7 +373,9 @@ int bsa_select_attn_decode_static(const void *q, int32_t num_q_heads, const bsa_
  * non-sentinel blocks in kv_idx[t][j / (H_q/H_kv)] (idx_stride entries per
  * (tile, KV head), ascending, -1 padded) whose position is <= r;
  * kv_idx == NULL attends to every block up to the diagonal (dense causal
- * baseline).  kv: batch 1, token-major bf16 [num_rows][H_kv][D] with
+ * baseline).  A (tile, KV head) list ends at its first entry that is
+ * negative or past the tile; a row with no block to attend to comes out NaN
+ * (the softmax over an empty set).  kv: batch 1, token-major bf16 [num_rows][H_kv][D] with
  * page_size == tile_rows == 64 and block_table NULL.  q [num_rows][H_q][D]
  * bf16; out [num_rows][H_q][D] float32.  Matrix-core kernel (bf16 Q.K^T,
  * fp16 P.V, fp32 accumulation; V must lie in the fp16 range: a finite value

@@ -458,6 +458,32 @@ def test_tile_attention_value_beyond_fp16_range_is_not_silent(dev):
     assert np.max(np.abs(out[mask] - ref[mask])) <= ATTN_ABS["bf16"]
 
 
+def test_tile_attention_empty_and_short_block_lists(dev):
+    """Rows with nothing to attend to: a tile whose kv_idx row holds no
+    block (all -1) comes out NaN, the softmax over an empty set, exactly
+    where the oracle's does; a row cut short by an entry past the diagonal
+    ends there; every other row matches the oracle."""
+    from block_sparse_attention_chunk_amd import ops
+    pc = synth.router_prefill(cid=3, T=200, num_q_heads=4, num_kv_heads=2, k=2, groups=2, tied_groups=(),
+                              rms_heads=())
+    n_tiles = (pc.T + 63) // 64
+    kv_idx = np.full((n_tiles, 2, 3), -1, np.int32)
+    kv_idx[1, 0, :2] = [0, 1]
+    kv_idx[2, 1, 0] = 2
+    kv_idx[3, 0, :3] = [1, 3, 4]           # block 4 lies past tile 3: the list ends before it
+    kv_idx[3, 1, :1] = [0]
+    log("tile attention with empty and short block lists")
+    kv = ops.KVCache(ops.upload(pc.k, dev), ops.upload(pc.v, dev),
+                     torch.tensor([pc.T], dtype=torch.int32, device=dev), pc.block, token_major=True)
+    out = _np(ops.sparse_attn_tile_prefill(ops.upload(pc.q, dev), kv, torch.tensor(kv_idx, device=dev)))
+    torch.cuda.synchronize()
+    ref = oracle.tile_attn(pc.q, pc.k, pc.v, num_kv_heads=2, block_size=64, tile_rows=64, kv_idx=kv_idx)
+    assert np.array_equal(np.isnan(out), np.isnan(ref))
+    assert np.isnan(out[0:64]).all() and np.isnan(out[64:128, 2:4]).all()
+    fin = ~np.isnan(ref)
+    assert fin.sum() > 0 and np.max(np.abs(out[fin] - ref[fin])) <= ATTN_ABS["bf16"]
+
+
 def _random_prefill_config(i):
     """The i-th seeded router-prefill configuration: length (ragged), KV
     heads, group size, k, rho, quantile and scoring drawn together."""
