@@ -326,19 +326,33 @@ __global__ __launch_bounds__(64 * G) void tile_prefill_kernel(const uint16_t *__
         if (ii + 1 < nb) step(ii + 1, stage1, stage2, stage0);
         if (ii + 2 < nb) step(ii + 2, stage2, stage0, stage1);
     }
-    wait_vmcnt<0>();  // no copy may still target LDS when the workgroup ends
-    // normalise and write: lane holds O^T[dim 16dt + 4*G4 + i][row 16rt + n16]
+    wait_vmcnt<0>();  // this wave's copies have landed
+    stage_barrier();  // and every other wave's: the ring is free
+    // Normalise and write.  Lane (n16, G4) holds O^T[dim 16dt + 4*G4 + i][row
+    // 16rt + n16]: written straight out, each store would cover 64 bytes of 16
+    // rows.  Staged per row tile through this wave's corner of the ring (16
+    // rows, padded stride), each store covers two whole 512-byte rows instead
+    // (measured 2 % faster at 131,072 tokens; the output is 1.9 GB of fp32).
+    {
+        constexpr int RS = kPfD + 4;  // floats per staged row
+        static_assert(3 * 16 * RS * 4 <= kPfStageBytes, "three waves' rows per stage");
+        float *stg = reinterpret_cast<float *>(w < 3 ? stage0 : (w < 6 ? stage1 : stage2)) + (w % 3) * (16 * RS);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const float l = lsum[rt][0];  // every row of the sum tile holds the row's total
-        const int r = rbase + 16 * rt + n16;
-        if (r < rows) {
-            const float inv = 1.0f / l;
-            float *orow = out + ((int64_t)r * hq + j) * kPfD;
+        for (int rt = 0; rt < 2; ++rt) {
+            const float inv = 1.0f / lsum[rt][0];  // every row of the sum tile holds the row's total
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 const f32x4 v = o[dt][rt] * inv;
-                *reinterpret_cast<float4 *>(orow + 16 * dt + 4 * G4) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4 *>(stg + n16 * RS + 16 * dt + 4 * G4) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+            // (a wave's LDS accesses run in order: these reads see the writes
+            // above, and the next row tile's writes follow these reads)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 2 * i + (lane >> 5), col = (lane & 31) * 4;
+                const float4 x = *reinterpret_cast<const float4 *>(stg + row * RS + col);
+                const int r = rbase + 16 * rt + row;
+                if (r < rows) *reinterpret_cast<float4 *>(out + ((int64_t)r * hq + j) * kPfD + col) = x;
             }
         }
     }
