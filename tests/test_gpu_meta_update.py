@@ -120,3 +120,72 @@ def test_variable_chunks_last_chunk_grows(dev):
     torch.cuda.synchronize()
     _same(meta, ref, [n])
     _vs_oracle(meta, case, [L], starts, case.num_chunks)
+
+
+def _random_update_config(i):
+    """The i-th seeded incremental-update case: chunking (fixed pages of 16,
+    32 or 64 tokens, or variable chunks of 4-60 tokens), batch, heads, head
+    dim, dtype, new lengths and the tokens appended per sequence."""
+    r = np.random.default_rng(8000 + i)
+    batch = int(r.integers(1, 5))
+    L = r.integers(1, 3000, size=batch)
+    a = np.minimum(r.integers(0, 300, size=batch), L - 1)      # at least one token was there before
+    return dict(batch=batch, hkv=int(r.choice([1, 2, 4])), d=int(r.choice([64, 128])),
+                f32=bool(r.integers(0, 2)), page=int(r.choice([16, 32, 64])), variable=bool(i % 2),
+                L=L.astype(np.int32), L0=(L - a).astype(np.int32))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_randomized_updates(dev, i):
+    """Seeded appends of 0-299 tokens per sequence: the chunks an update
+    recomputes match a full rebuild bit for bit and the oracle's metadata of
+    the grown cache (kmin / kmax bit-exact, centroid within the fp32 bound)."""
+    from block_sparse_attention_chunk_amd import ops
+    c = _random_update_config(i)
+    B, L, L0 = c["batch"], c["L"], c["L0"]
+    page = 16 if c["variable"] else c["page"]
+    log(f"random update {i}: {c}")
+    case = synth.make_decode(8100 + i, batch=B, seq_lens=L, num_q_heads=c["hkv"], num_kv_heads=c["hkv"],
+                             head_dim=c["d"], page_size=page, dtype="f32" if c["f32"] else "bf16",
+                             name=f"update-{i}")
+    from_len = torch.tensor(L0, dtype=torch.int32, device=dev)
+    if not c["variable"]:
+        meta = ops.build_chunk_meta(_kv(ops, case, dev, L0))
+        touched = int(np.max((L - L0 + page - 1) // page + 1))
+        kv = _kv(ops, case, dev, L)
+        ops.update_chunk_meta(kv, meta, from_len=from_len, max_touched=min(touched, kv.max_pages))
+        ref = ops.build_chunk_meta(kv)
+        torch.cuda.synchronize()
+        _same(meta, ref, (L + page - 1) // page)
+        _vs_oracle(meta, case, L)
+        return
+    # variable chunks: the grown layout, and the old one (its chunks that start
+    # before the old length, the last one cut there)
+    r = np.random.default_rng(8500 + i)
+    new, old = [], []
+    for b in range(B):
+        s = [0]
+        while s[-1] < L[b]:
+            s.append(min(int(L[b]), s[-1] + int(r.integers(4, 61))))
+        s = np.asarray(s, np.int32)
+        n0 = int(np.searchsorted(s, L0[b], side="left"))        # chunks starting before L0
+        o = np.concatenate([s[:n0], [L0[b]]]).astype(np.int32)
+        new.append(s)
+        old.append(o)
+    synth.with_chunks(case, new)
+    starts, num = case.chunk_starts, case.num_chunks
+    mc = starts.shape[1] - 1
+    st0 = np.zeros_like(starts)
+    num0 = np.array([len(o) - 1 for o in old], np.int32)
+    for b, o in enumerate(old):
+        st0[b, :len(o)] = o
+        st0[b, len(o):] = o[-1]
+    touched = int(max(len(new[b]) - 1 - (len(old[b]) - 2) for b in range(B)))
+    meta = ops.build_chunk_meta(_kv(ops, case, dev, L0), ops.Chunks(ops.upload(st0, dev), ops.upload(num0, dev)))
+    kv = _kv(ops, case, dev, L)
+    ch = ops.Chunks(ops.upload(starts, dev), ops.upload(num, dev))
+    ops.update_chunk_meta(kv, meta, chunks=ch, from_len=from_len, max_touched=min(touched, mc))
+    ref = ops.build_chunk_meta(kv, ch)
+    torch.cuda.synchronize()
+    _same(meta, ref, num)
+    _vs_oracle(meta, case, L, starts, num)
