@@ -45,6 +45,10 @@ MUTANTS = {
     "expansion-swapped": ("int keep = triggered[t] ? width : k;", "int keep = triggered[t] ? k : width;"),
     "tile-diagonal-hidden": ("int v = last / block_size + 1;", "int v = last / block_size;"),
     "causal-leak": ("if (p > r) break;", "if (p > r + 1) break;"),
+    "tile-score-first-row": ("for (int r = r0; r < r1; ++r)", "for (int r = r0; r < r0 + 1; ++r)"),
+    "bos-forced-second-page": ("if (n > 0 && bos && !taken[0]) { taken[0] = 1; keep[m++] = 0; }",
+                               "if (n > 1 && bos && !taken[1]) { taken[1] = 1; keep[m++] = 1; }"),
+    "kmax-skips-last-token": ("if (x > hi) hi = x;", "if (x > hi && t + 1 < e) hi = x;"),
 }
 
 
