@@ -49,6 +49,10 @@ MUTANTS = {
     "bos-forced-second-page": ("if (n > 0 && bos && !taken[0]) { taken[0] = 1; keep[m++] = 0; }",
                                "if (n > 1 && bos && !taken[1]) { taken[1] = 1; keep[m++] = 1; }"),
     "kmax-skips-last-token": ("if (x > hi) hi = x;", "if (x > hi && t + 1 < e) hi = x;"),
+    "decode-skips-first-selected": ("for (int i = 0; i < cnt; ++i) {\n                    int s, e;",
+                                    "for (int i = 1; i < cnt; ++i) {\n                    int s, e;"),
+    "expansion-unsorted": ("qsort(dst, keep, sizeof(int32_t), int_cmp);", ""),
+    "sentinel-zero": ("for (int i = keep; i < width; ++i) dst[i] = -1;", "for (int i = keep; i < width; ++i) dst[i] = 0;"),
 }
 
 
