@@ -133,11 +133,13 @@ constexpr int kMaxItemsPerSplit = 2048;  // the fused selection keeps one split'
 int resolve_splits(const bsa_kv *kv, int32_t max_items, int32_t num_splits) {
     if (num_splits > 0) return num_splits;
     const int bh = kv->batch * kv->num_kv_heads;
-    // ~192 workgroups: the fused kernel repeats the selection in every split,
-    // so few, long splits pay off as long as most compute units get one
-    // (measured at 16 x 32K tokens: 3 splits 26.7 us against 8 splits 28.5 us
-    // fused, the unfused decode kernel flat; at 16 x 64 heads 2 splits best)
-    int s = (192 + bh - 1) / bh;
+    // ~256 workgroups, one per compute unit: the fused kernel repeats the
+    // selection in every split, so few, long splits pay off as long as every
+    // compute unit gets one (measured decode steps at 16 x 32K tokens, 4 KV
+    // heads: 4 splits 50.2 us, 3 splits 51.0 us, 8 splits slower; 8 KV heads:
+    // 2 splits 88.6 us, 3 splits 94.6 us; one sequence: 32 splits, the cap
+    // below, best of 8 to 64)
+    int s = (256 + bh - 1) / bh;
     const int cap = (max_items + 7) / 8;                // at least ~8 items per workgroup
     if (s > cap) s = cap;
     const int floor_s = (max_items + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit;
